@@ -1,0 +1,255 @@
+"""CPU reference (oracle) for grouped-query attention and grouped query experts.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+baseline leg may import this module. The HIP library never calls it and shares
+no code with it; it exists to decide, element by element, whether the GPU path
+computes the right thing.
+
+Everything is plain NumPy in float64. Inputs (float32 or bfloat16 values that
+were handed to the GPU) are upcast losslessly and no intermediate is rounded.
+Each step is written as the pages define it, without blocking, fusion or
+reordering:
+
+* GQA (ml-canon "56 GQA / MQA", section on the PyTorch GQA function; IBM Think
+  "What is grouped query attention (GQA)?", discussion of scaled dot-product
+  attention): the g key/value heads are replicated explicitly so that each of
+  the h query heads sees its group's head, then scores = q k^T / sqrt(d),
+  a softmax over keys, and the probability-weighted sum of value rows.
+* The causal (autoregressive) mask: a query at position t only sees key
+  positions 0..t (IBM Think page, on autoregressive decoders attending to
+  previous tokens).
+* Decode over a KV cache (aiunderstanding.org "Attention aux requetes
+  groupees", section "Plongee profonde"): one new query per sequence attends
+  to every cached key of its sequence.
+* GQE routing (gist.science explainer of "Grouped Query Experts: Mixture-of-
+  Experts on GQA Self-Attention", section "Architecture et Routage"): for each
+  token a router keeps k query-head experts inside every KV group, the KV path
+  stays dense, and the selected outputs are weighted by the router
+  probabilities renormalised over the k selected experts.
+* The KV-cache size law (ml-canon page, section on where the KV-cache saving
+  comes from): bytes grow as 2 * L * n_kv * d_h * T.
+
+Readings where the pages are silent (all listed in the design notes):
+contiguous head-to-group map (head i uses KV head i // (h/g)); causal mask
+aligned at the top-left with the diagonal visible; stable softmax by row-max
+subtraction; router ties go to the lower head index, and the k indices are
+returned in rank order; unselected heads output zero.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "kv_head_of",
+    "replicate_kv",
+    "scores",
+    "causal_mask",
+    "softmax",
+    "gqa_ref",
+    "gqa_ref_row",
+    "gqa_decode_ref",
+    "gqe_topk_ref",
+    "gqe_ref",
+    "kv_cache_bytes",
+    "gqe_active_query_heads",
+]
+
+
+def _f64(x) -> np.ndarray:
+    """Lossless upcast of a NumPy array or a torch tensor to float64."""
+    if hasattr(x, "detach"):  # torch tensor, possibly bfloat16
+        x = x.detach().to("cpu")
+        import torch  # local: only needed when torch tensors are handed in
+
+        x = x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def kv_head_of(i: int, h: int, g: int) -> int:
+    """KV head used by query head ``i``: contiguous blocks of h/g query heads.
+
+    ml-canon page, PyTorch GQA function (repeat-interleave along the head
+    axis); freenetmedia "Grouped-Query Attention", section "Jak dzialaja ...":
+    with 8 query heads in 2 groups, heads 0-3 share the first K/V set and heads
+    4-7 the second.
+    """
+    if h % g:
+        raise ValueError(f"g={g} must divide h={h}")
+    return i // (h // g)
+
+
+def replicate_kv(x: np.ndarray, h: int) -> np.ndarray:
+    """[B,g,T,d] -> [B,h,T,d], each KV head repeated h/g times in place
+    (the explicit replication of the ml-canon GQA function)."""
+    g = x.shape[1]
+    if h % g:
+        raise ValueError(f"g={g} must divide h={h}")
+    return np.repeat(x, h // g, axis=1)
+
+
+def scores(q: np.ndarray, k_rep: np.ndarray, scale: float) -> np.ndarray:
+    """Scaled dot products q k^T * scale, [..., Tq, Tk] (IBM Think page,
+    scaled dot-product attention with factor 1/sqrt(d_k))."""
+    return np.matmul(q, np.swapaxes(k_rep, -1, -2)) * scale
+
+
+def causal_mask(Tq: int, Tk: int) -> np.ndarray:
+    """Boolean [Tq, Tk], True where key j is visible to query t (j <= t)."""
+    t = np.arange(Tq)[:, None]
+    j = np.arange(Tk)[None, :]
+    return j <= t
+
+
+def softmax(s: np.ndarray, visible: np.ndarray | None = None) -> np.ndarray:
+    """Softmax over the last axis (IBM Think page: weights in [0, 1] that sum
+    to one). Masked entries get weight 0; the row max is subtracted first,
+    which changes no exact value."""
+    if visible is not None:
+        s = np.where(visible, s, -np.inf)
+    m = np.max(s, axis=-1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m)
+    den = np.sum(e, axis=-1, keepdims=True)
+    return np.divide(e, den, out=np.zeros_like(e), where=den > 0)
+
+
+def gqa_ref(q, k, v, causal: bool = True, scale: float | None = None,
+            return_probs: bool = False):
+    """GQA prefill. q [B,h,T,d], k/v [B,g,T,d] -> out [B,h,T,d] (float64).
+
+    Follows the ml-canon GQA function step by step (replicate KV, scores,
+    softmax, weighted sum of V) and adds the causal mask. One batch element at
+    a time bounds memory. With ``return_probs`` also returns the row sums of
+    the attention weights, [B,h,T].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, h, T, d = q.shape
+    if k.shape[0] != B or k.shape[2:] != (T, d) or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    vis = causal_mask(T, T) if causal else None
+    out = np.empty((B, h, T, d))
+    sums = np.empty((B, h, T)) if return_probs else None
+    for b in range(B):
+        kr = replicate_kv(k[b:b + 1], h)[0]
+        vr = replicate_kv(v[b:b + 1], h)[0]
+        p = softmax(scores(q[b], kr, scale), vis)
+        out[b] = np.matmul(p, vr)
+        if return_probs:
+            sums[b] = p.sum(axis=-1)
+    return (out, sums) if return_probs else out
+
+
+def gqa_ref_row(q, k, v, b: int, i: int, t: int, causal: bool = True,
+                scale: float | None = None) -> np.ndarray:
+    """One output row out[b, i, t, :] of :func:`gqa_ref`, computed on its own
+    (for sampled checks at sizes where the whole output is too costly)."""
+    d = q.shape[-1]
+    h, g = q.shape[1], k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kv = kv_head_of(i, h, g)
+    n = t + 1 if causal else k.shape[2]
+    qr = _f64(q[b, i, t])
+    kr = _f64(k[b, kv, :n])
+    vr = _f64(v[b, kv, :n])
+    p = softmax(kr @ qr * scale)
+    return p @ vr
+
+
+def gqa_decode_ref(q, k_cache, v_cache, lens, scale: float | None = None):
+    """Decode step. q [B,h,d], caches [B,g,T_max,d], lens [B] -> out [B,h,d].
+
+    The new token's query attends to every cached position below lens[b]
+    (the cache already holds the new token's key and value); positions at or
+    beyond lens[b] are never read. lens[b] = 0 gives a zero row.
+    """
+    q = _f64(q)
+    B, h, d = q.shape
+    g = k_cache.shape[1]
+    lens = np.asarray(lens.cpu() if hasattr(lens, "cpu") else lens).astype(np.int64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.zeros((B, h, d))
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        kr = replicate_kv(_f64(k_cache[b:b + 1, :, :n]), h)[0]   # [h,n,d]
+        vr = replicate_kv(_f64(v_cache[b:b + 1, :, :n]), h)[0]
+        s = scores(q[b][:, None, :], kr, scale)                   # [h,1,n]
+        out[b] = np.matmul(softmax(s), vr)[:, 0, :]
+    return out
+
+
+def gqe_topk_ref(logits, g: int, top_k: int):
+    """Router selection per (token, KV group).
+
+    logits [B,T,h] (float32 values) -> idx [B,T,g,k] int32 global head indices
+    in rank order and gate [B,T,g,k] float64.
+
+    gist.science GQE explainer, section "Architecture et Routage": within each
+    group of h/g query-head experts the router keeps k; the selected outputs
+    are combined with the router probabilities renormalised over the k kept.
+    Order: higher logit first, equal logits by lower head index. The raw
+    float32 logits are compared (the upcast to float64 keeps order and ties).
+    Router probabilities are the softmax over the group's logits; the gate is
+    that probability divided by the sum over the selected experts.
+    """
+    lg = _f64(logits)
+    B, T, h = lg.shape
+    r = h // g
+    if h % g or not 1 <= top_k <= r:
+        raise ValueError("need g | h and 1 <= top_k <= h/g")
+    idx = np.empty((B, T, g, top_k), dtype=np.int32)
+    gate = np.empty((B, T, g, top_k))
+    for b in range(B):
+        for t in range(T):
+            for gam in range(g):
+                ell = lg[b, t, gam * r:(gam + 1) * r]
+                order = sorted(range(r), key=lambda e: (-ell[e], e))
+                sel = order[:top_k]
+                prob = softmax(ell)
+                w = prob[sel] / prob[sel].sum()
+                idx[b, t, gam] = [gam * r + e for e in sel]
+                gate[b, t, gam] = w
+    return idx, gate
+
+
+def gqe_ref(q, k, v, logits, top_k: int, causal: bool = True,
+            scale: float | None = None):
+    """GQE routed prefill -> (out [B,h,T,d] float64, idx, gate).
+
+    The keys and values stay dense (every selected row attends to all visible
+    keys of its group), so a selected head's row equals the dense GQA row,
+    multiplied by its gate; the rows of heads the router did not select are 0.
+    """
+    g = k.shape[1]
+    idx, gate = gqe_topk_ref(logits, g, top_k)
+    dense = gqa_ref(q, k, v, causal=causal, scale=scale)
+    out = np.zeros_like(dense)
+    B, T = idx.shape[0], idx.shape[1]
+    for b in range(B):
+        for t in range(T):
+            for gam in range(g):
+                for j in range(top_k):
+                    i = int(idx[b, t, gam, j])
+                    out[b, i, t] = gate[b, t, gam, j] * dense[b, i, t]
+    return out, idx, gate
+
+
+def kv_cache_bytes(B: int, n_kv: int, T: int, d: int, elt_bytes: int,
+                   layers: int = 1) -> int:
+    """KV-cache size: keys and values for each layer, KV head and token
+    (ml-canon page, section on where the KV-cache saving comes from)."""
+    return 2 * layers * n_kv * d * T * elt_bytes * B
+
+
+def gqe_active_query_heads(g: int, top_k: int, shared: int = 1) -> int:
+    """Query-attention computations per token in GQE: k routed experts in each
+    of the g groups, plus the always-active shared head(s) (gist.science GQE
+    explainer, section "Resultats Experimentaux")."""
+    return g * top_k + shared
