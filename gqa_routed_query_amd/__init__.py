@@ -1,0 +1,29 @@
+"""gqa_routed_query_amd: grouped-query attention (GQA) and grouped query
+experts (GQE) on AMD MI355X (gfx950).
+
+The compute path is the HIP library ``libgqa.so`` (C ABI, ``include/gqa.h``);
+this package only marshals torch tensors into its entry points:
+
+* :func:`gqa_prefill` -- GQA prefill, q [B,h,T,d], k/v [B,g,T,d].
+* :func:`gqa_decode` -- one decode step over a KV cache [B,g,T_max,d].
+* :func:`gqe_routed_prefill` -- GQE: top-k query-head experts per KV group
+  per token, dense K/V.
+
+torch provides device memory and the stream; every step of the computation
+runs in the library's kernels. Importing the package fails loudly when the
+library has not been built (``python -m gqa_routed_query_amd.build``).
+"""
+from ._binding import (  # noqa: F401
+    GQA_BF16,
+    GQA_F32,
+    GqaError,
+    abi_version,
+    gqa_decode,
+    gqa_decode_workspace_bytes,
+    gqa_kv_cache_bytes,
+    gqa_prefill,
+    gqe_routed_prefill,
+    last_error,
+    lib_path,
+    status_string,
+)

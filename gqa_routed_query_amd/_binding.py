@@ -1,0 +1,203 @@
+"""ctypes binding of libgqa.so: argument marshalling only.
+
+Each wrapper checks the torch tensors it is given (device, dtype, layout,
+shape), allocates outputs when the caller passes none, and calls the C entry
+point of the same name with raw device pointers and the current HIP stream.
+No attention arithmetic happens here, and there is no fallback: if the library
+is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG_DIR, "libgqa.so")
+
+GQA_F32 = 0
+GQA_BF16 = 1
+_STATUS = {0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_UNSUPPORTED",
+           3: "GQA_ERR_WORKSPACE", 4: "GQA_ERR_NO_DEVICE", 5: "GQA_ERR_HIP"}
+
+
+class GqaError(RuntimeError):
+    """A libgqa entry point returned a non-OK status."""
+
+    def __init__(self, fn: str, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {detail}")
+
+
+def _load():
+    if not os.path.exists(lib_path):
+        raise ImportError(
+            f"{lib_path} is not built; run `python -m gqa_routed_query_amd.build` "
+            "(hipcc, gfx950)")
+    lib = ctypes.CDLL(lib_path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.gqa_abi_version.restype = i32
+    lib.gqa_abi_version.argtypes = []
+    lib.gqa_prefill.restype = i32
+    lib.gqa_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.gqa_decode_workspace_bytes.restype = sz
+    lib.gqa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.gqa_decode.restype = i32
+    lib.gqa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                               vp, sz, vp]
+    lib.gqe_routed_prefill.restype = i32
+    lib.gqe_routed_prefill.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32,
+                                       i32, i32, i32, f32, i32, vp]
+    lib.gqa_kv_cache_bytes.restype = ctypes.c_uint64
+    lib.gqa_kv_cache_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.gqa_status_string.restype = ctypes.c_char_p
+    lib.gqa_status_string.argtypes = [i32]
+    lib.gqa_last_error.restype = ctypes.c_char_p
+    lib.gqa_last_error.argtypes = []
+    return lib
+
+
+_lib = _load()
+
+_DT = {torch.float32: GQA_F32, torch.bfloat16: GQA_BF16}
+
+
+def abi_version() -> int:
+    return int(_lib.gqa_abi_version())
+
+
+def status_string(status: int) -> str:
+    return _lib.gqa_status_string(status).decode()
+
+
+def last_error() -> str:
+    return _lib.gqa_last_error().decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise GqaError(fn, status, last_error())
+
+
+def _dt(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"{name}: dtype {t.dtype} is not float32 or bfloat16")
+    return _DT[t.dtype]
+
+
+def _dev(*tensors):
+    dev = tensors[0].device
+    for t in tensors:
+        if t.device.type != "cuda":
+            raise ValueError("libgqa tensors must live on the GPU")
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+        if not t.is_contiguous():
+            raise ValueError("libgqa tensors must be contiguous")
+    return dev
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def gqa_kv_cache_bytes(B: int, n_kv: int, T: int, d: int, dtype=torch.bfloat16) -> int:
+    """Bytes of a one-layer KV cache: 2 * n_kv * d * T * sizeof(dtype) * B."""
+    return int(_lib.gqa_kv_cache_bytes(B, n_kv, T, d, _DT[dtype]))
+
+
+def gqa_decode_workspace_bytes(B: int, h: int, g: int, T_max: int, d: int) -> int:
+    return int(_lib.gqa_decode_workspace_bytes(B, h, g, T_max, d))
+
+
+def gqa_prefill(q, k, v, causal: bool = True, scale: float | None = None, out=None,
+                out_dtype=None):
+    """GQA prefill. q [B,h,T,d], k/v [B,g,T,d] -> out [B,h,T,d]."""
+    dev = _dev(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q [B,h,T,d] and k, v [B,g,T,d]")
+    B, h, T, d = q.shape
+    if k.shape[0] != B or k.shape[2:] != (T, d):
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    g = k.shape[1]
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, h, T, d), dtype=out_dtype, device=dev)
+    elif out.shape != q.shape or out.dtype != out_dtype:
+        raise ValueError("out must be [B,h,T,d] of out_dtype")
+    _dev(q, out)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = _lib.gqa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          B, h, g, T, d, _dt(q, "q"), _dt(out, "out"), scale,
+                          int(bool(causal)), _stream(dev))
+    _check("gqa_prefill", st)
+    return out
+
+
+def gqa_decode(q, k_cache, v_cache, lens, scale: float | None = None, out=None,
+               out_dtype=None, workspace=None):
+    """GQA decode. q [B,h,d], caches [B,g,T_max,d], lens [B] int32 -> out [B,h,d]."""
+    dev = _dev(q, k_cache, v_cache, lens)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,h,d] and caches [B,g,T_max,d]")
+    B, h, d = q.shape
+    if k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError("cache shape does not match q")
+    if lens.dtype != torch.int32 or lens.shape != (B,):
+        raise ValueError("lens must be int32 [B]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    g, T_max = k_cache.shape[1], k_cache.shape[2]
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, h, d), dtype=out_dtype, device=dev)
+    elif out.shape != q.shape or out.dtype != out_dtype:
+        raise ValueError("out must be [B,h,d] of out_dtype")
+    _dev(q, out)
+    need = gqa_decode_workspace_bytes(B, h, g, T_max, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = _lib.gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lens.data_ptr(),
+                         out.data_ptr(), B, h, g, T_max, d, _dt(q, "q"), _dt(out, "out"),
+                         scale, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                         _stream(dev))
+    _check("gqa_decode", st)
+    return out
+
+
+def gqe_routed_prefill(q, k, v, router_logits, top_k: int, causal: bool = True,
+                       scale: float | None = None, out=None, out_dtype=None):
+    """GQE routed prefill -> (out [B,h,T,d], idx [B,T,g,k] int32, gate [B,T,g,k] fp32)."""
+    dev = _dev(q, k, v, router_logits)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q [B,h,T,d] and k, v [B,g,T,d]")
+    B, h, T, d = q.shape
+    g = k.shape[1]
+    if k.shape[0] != B or k.shape[2:] != (T, d):
+        raise ValueError("k/v shape does not match q")
+    if router_logits.dtype != torch.float32 or router_logits.shape != (B, T, h):
+        raise ValueError("router_logits must be float32 [B,T,h]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, h, T, d), dtype=out_dtype, device=dev)
+    elif out.shape != q.shape or out.dtype != out_dtype:
+        raise ValueError("out must be [B,h,T,d] of out_dtype")
+    _dev(q, out)
+    kk = max(int(top_k), 1)
+    idx = torch.empty((B, T, g, kk), dtype=torch.int32, device=dev)
+    gate = torch.empty((B, T, g, kk), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = _lib.gqe_routed_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 router_logits.data_ptr(), int(top_k), out.data_ptr(),
+                                 idx.data_ptr(), gate.data_ptr(), B, h, g, T, d,
+                                 _dt(q, "q"), _dt(out, "out"), scale, int(bool(causal)),
+                                 _stream(dev))
+    _check("gqe_routed_prefill", st)
+    return out, idx, gate

@@ -1,0 +1,208 @@
+// C ABI of libgqa: argument checks, dispatch and launches on the caller's
+// stream. Declarations and the contract of each entry point are in gqa.h.
+#include "gqa.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gqa_status fail(gqa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int dt) { return dt == GQA_F32 || dt == GQA_BF16; }
+
+// Checks shared by the prefill-shaped entry points.
+gqa_status check_prefill_shape(const void* q, const void* k, const void* v, const void* out,
+                               int B, int h, int g, int T, int d, int in_dt, int out_dt,
+                               float scale, int causal) {
+  if (B < 0 || T < 0) return fail(GQA_ERR_INVALID_ARG, "B=%d and T=%d must be >= 0", B, T);
+  if (h < 1 || g < 1) return fail(GQA_ERR_INVALID_ARG, "h=%d and g=%d must be >= 1", h, g);
+  if (h % g != 0) return fail(GQA_ERR_INVALID_ARG, "g=%d must divide h=%d", g, h);
+  if (d < 1) return fail(GQA_ERR_INVALID_ARG, "d=%d must be >= 1", d);
+  if (!valid_dtype(in_dt) || !valid_dtype(out_dt))
+    return fail(GQA_ERR_INVALID_ARG, "unknown dtype (in %d, out %d)", in_dt, out_dt);
+  if (!(std::isfinite(scale) && scale > 0.0f))
+    return fail(GQA_ERR_INVALID_ARG, "scale=%g must be finite and > 0", (double)scale);
+  if (causal != 0 && causal != 1) return fail(GQA_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
+  if ((long long)h * T >= (1ll << 31))
+    return fail(GQA_ERR_INVALID_ARG, "h*T=%lld exceeds the 2^31 row limit", (long long)h * T);
+  if (B == 0 || T == 0) return GQA_OK;
+  if (!q || !k || !v || !out) return fail(GQA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(GQA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (in_dt == GQA_BF16 && !gqa::attn_bf16_supports(d))
+    return fail(GQA_ERR_UNSUPPORTED, "bf16 prefill supports d in {64, 128}, got %d", d);
+  if (in_dt == GQA_F32 && !gqa::attn_f32_supports(d))
+    return fail(GQA_ERR_UNSUPPORTED, "fp32 prefill supports d in {16, 32, 64, 128}, got %d", d);
+  return GQA_OK;
+}
+
+gqa_status check_device() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    return fail(GQA_ERR_NO_DEVICE, "no HIP device visible");
+  }
+  return GQA_OK;
+}
+
+gqa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return GQA_OK;
+  return fail(GQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct DecodeLayout {
+  int chunk, n_split;
+  size_t acc_bytes, ml_bytes, total;
+};
+
+DecodeLayout decode_layout(int B, int h, int g, int T_max, int d) {
+  DecodeLayout L{};
+  L.chunk = gqa::decode_chunk(B, h, g, T_max);
+  L.n_split = T_max > 0 ? (T_max + L.chunk - 1) / L.chunk : 1;
+  if (L.n_split <= 1) return L;
+  const size_t rows = (size_t)B * h * L.n_split;
+  L.acc_bytes = (rows * d * sizeof(float) + 255) & ~(size_t)255;
+  L.ml_bytes = rows * 2 * sizeof(float);
+  L.total = L.acc_bytes + L.ml_bytes;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_abi_version(void) { return 1; }
+
+const char* gqa_status_string(gqa_status s) {
+  switch (s) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_INVALID_ARG: return "invalid argument";
+    case GQA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GQA_ERR_WORKSPACE: return "workspace too small";
+    case GQA_ERR_NO_DEVICE: return "no HIP device";
+    case GQA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* gqa_last_error(void) { return g_last_error; }
+
+uint64_t gqa_kv_cache_bytes(int B, int n_kv, int T, int d, gqa_dtype dtype) {
+  if (B < 0 || n_kv < 0 || T < 0 || d < 0 || !valid_dtype(dtype)) return 0;
+  const uint64_t elt = dtype == GQA_BF16 ? 2 : 4;
+  return 2ull * (uint64_t)n_kv * (uint64_t)d * (uint64_t)T * elt * (uint64_t)B;
+}
+
+gqa_status gqa_prefill(const void* q, const void* k, const void* v, void* out, int B, int h, int g,
+                       int T, int d, gqa_dtype in_dtype, gqa_dtype out_dtype, float scale, int causal,
+                       void* stream) {
+  g_last_error[0] = '\0';
+  gqa_status s = check_prefill_shape(q, k, v, out, B, h, g, T, d, in_dtype, out_dtype, scale, causal);
+  if (s != GQA_OK || B == 0 || T == 0) return s;
+  if ((s = check_device()) != GQA_OK) return s;
+  gqa::AttnParams p{};
+  p.q = q; p.k = k; p.v = v; p.out = out;
+  p.B = B; p.h = h; p.g = g; p.T = T; p.d = d;
+  p.R = h / g;
+  p.scale = scale;
+  p.causal = causal;
+  p.out_bf16 = out_dtype == GQA_BF16;
+  auto st = static_cast<hipStream_t>(stream);
+  const hipError_t e = in_dtype == GQA_BF16 ? gqa::launch_attn_bf16(p, st) : gqa::launch_attn_f32(p, st);
+  return hip_status(e, "gqa_prefill launch");
+}
+
+size_t gqa_decode_workspace_bytes(int B, int h, int g, int T_max, int d) {
+  if (B <= 0 || h < 1 || g < 1 || h % g || T_max <= 0 || d <= 0) return 0;
+  return decode_layout(B, h, g, T_max, d).total;
+}
+
+gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* lens,
+                      void* out, int B, int h, int g, int T_max, int d, gqa_dtype in_dtype,
+                      gqa_dtype out_dtype, float scale, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  g_last_error[0] = '\0';
+  if (B < 0 || T_max < 0) return fail(GQA_ERR_INVALID_ARG, "B=%d and T_max=%d must be >= 0", B, T_max);
+  if (h < 1 || g < 1) return fail(GQA_ERR_INVALID_ARG, "h=%d and g=%d must be >= 1", h, g);
+  if (h % g != 0) return fail(GQA_ERR_INVALID_ARG, "g=%d must divide h=%d", g, h);
+  if (d < 1) return fail(GQA_ERR_INVALID_ARG, "d=%d must be >= 1", d);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(GQA_ERR_INVALID_ARG, "unknown dtype (in %d, out %d)", in_dtype, out_dtype);
+  if (!(std::isfinite(scale) && scale > 0.0f))
+    return fail(GQA_ERR_INVALID_ARG, "scale=%g must be finite and > 0", (double)scale);
+  if ((long long)g * T_max >= (1ll << 31))
+    return fail(GQA_ERR_INVALID_ARG, "g*T_max=%lld exceeds the 2^31 row limit", (long long)g * T_max);
+  if (B == 0) return GQA_OK;
+  if (!q || !out || !lens) return fail(GQA_ERR_INVALID_ARG, "null q, out or lens pointer");
+  if (T_max > 0 && (!k_cache || !v_cache)) return fail(GQA_ERR_INVALID_ARG, "null cache pointer");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(GQA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (in_dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "decode supports bf16 caches only");
+  if (!gqa::decode_supports(d)) return fail(GQA_ERR_UNSUPPORTED, "decode supports d in {64, 128}, got %d", d);
+  if (h / g > 64) return fail(GQA_ERR_UNSUPPORTED, "decode supports h/g <= 64, got %d", h / g);
+  const DecodeLayout L = decode_layout(B, h, g, T_max > 0 ? T_max : 1, d);
+  if (workspace_bytes < L.total)
+    return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, L.total);
+  if (L.total && (!workspace || !aligned16(workspace)))
+    return fail(GQA_ERR_INVALID_ARG, "workspace must be a 16-byte aligned device pointer");
+  gqa_status s = check_device();
+  if (s != GQA_OK) return s;
+  gqa::DecodeParams p{};
+  p.q = q; p.k_cache = k_cache; p.v_cache = v_cache; p.lens = lens; p.out = out;
+  p.B = B; p.h = h; p.g = g; p.T_max = T_max; p.d = d;
+  p.chunk = L.chunk;
+  p.n_split = L.n_split;
+  p.part_acc = L.total ? static_cast<float*>(workspace) : nullptr;
+  p.part_ml = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.acc_bytes) : nullptr;
+  p.scale = scale;
+  p.out_bf16 = out_dtype == GQA_BF16;
+  return hip_status(gqa::launch_decode(p, static_cast<hipStream_t>(stream)), "gqa_decode launch");
+}
+
+gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v, const float* router_logits,
+                              int top_k, void* out, int32_t* topk_idx, float* topk_gate, int B, int h,
+                              int g, int T, int d, gqa_dtype in_dtype, gqa_dtype out_dtype, float scale,
+                              int causal, void* stream) {
+  g_last_error[0] = '\0';
+  gqa_status s = check_prefill_shape(q, k, v, out, B, h, g, T, d, in_dtype, out_dtype, scale, causal);
+  if (s != GQA_OK) return s;
+  const int r = h / g;
+  if (top_k < 1 || top_k > r) return fail(GQA_ERR_INVALID_ARG, "top_k=%d must be in [1, h/g=%d]", top_k, r);
+  if (r > 64) return fail(GQA_ERR_UNSUPPORTED, "routing supports h/g <= 64, got %d", r);
+  if (B == 0 || T == 0) return GQA_OK;
+  if (!router_logits || !topk_idx || !topk_gate)
+    return fail(GQA_ERR_INVALID_ARG, "null router_logits, topk_idx or topk_gate pointer");
+  if ((s = check_device()) != GQA_OK) return s;
+  auto st = static_cast<hipStream_t>(stream);
+  gqa::RouterParams rp{router_logits, topk_idx, topk_gate, B, T, h, g, top_k};
+  if ((s = hip_status(gqa::launch_router(rp, st), "gqe router launch")) != GQA_OK) return s;
+  gqa::AttnParams p{};
+  p.q = q; p.k = k; p.v = v; p.out = out;
+  p.idx = topk_idx;
+  p.gate = topk_gate;
+  p.B = B; p.h = h; p.g = g; p.T = T; p.d = d;
+  p.R = top_k;
+  p.scale = scale;
+  p.causal = causal;
+  p.out_bf16 = out_dtype == GQA_BF16;
+  p.zero_unselected = 1;
+  const hipError_t e = in_dtype == GQA_BF16 ? gqa::launch_attn_bf16(p, st) : gqa::launch_attn_f32(p, st);
+  return hip_status(e, "gqe routed attention launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,335 @@
+// Grouped-query attention prefill, bf16 inputs, fp32 accumulation, on the
+// gfx950 matrix cores. One kernel serves dense GQA and routed GQE.
+//
+// What is computed (ml-canon "56 GQA / MQA", PyTorch GQA function; IBM Think
+// "What is grouped query attention (GQA)?", scaled dot-product attention):
+// for every query head i of KV group gamma = i / (h/g), out = softmax(q k^T *
+// scale) v over the keys of that group, with the causal mask (key j visible to
+// query t iff j <= t) when requested. Routed GQE (gist.science explainer of
+// "Grouped Query Experts", section "Architecture et Routage") runs the same
+// attention for the (token, head) pairs its router kept, on dense K/V, and
+// multiplies each row by its gate.
+//
+// Design for CDNA4:
+//  * A workgroup owns 256 attention rows of one (batch, KV group): rows are
+//    (token, slot) pairs in token-major order, so one K/V tile staged in LDS is
+//    shared by every query head of the group (the GQA reuse), and a routed
+//    problem is just a shorter row list with a head lookup per row.
+//  * 8 waves x 32 rows. Scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_bf16 so that each lane ends up owning one query row
+//    (column l%32); the probabilities are then already in the B-operand layout
+//    of O^T += V^T P^T, and the online-softmax statistics of a row live in two
+//    lanes (l and l^32) -- one cross-lane max per tile, sums combined once.
+//  * K tiles are read from LDS with 16-byte reads in the A-operand layout; V
+//    stays row-major in LDS and is transposed by ds_read_b64_tr_b16.
+//  * Double-buffered LDS: the next tile's global loads are in flight while the
+//    current tile is multiplied; one barrier per tile.
+//  * Causal grids are issued heaviest-first; (batch, group) is the fastest
+//    varying part of the block index, so with B*g a multiple of 8 all tiles of
+//    one group land on one XCD and share its L2.
+#include "common.h"
+#include "launch.h"
+
+namespace gqa {
+namespace {
+
+constexpr int kBN = 64;                               // keys per KV tile
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowsPerBlock = kWaves * 32;
+
+template <int D>
+struct Tile {
+  static constexpr int kPitch = D + 8;    // 16-byte pad: A-operand reads of 16 rows hit distinct banks
+  static constexpr int vPitch = D + 32;   // 64-byte pad: transposing reads of 4 rows hit distinct banks
+  static constexpr int kElems = kBN * kPitch;
+  static constexpr int vElems = kBN * vPitch;
+  static constexpr int kCPR = D / 8;      // 16-byte chunks per row
+  static constexpr int kLoads = kBN * kCPR / kThreads;
+  static_assert(kBN * kCPR % kThreads == 0, "tile must split evenly over the block");
+};
+
+struct KArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  void* out;
+  const int32_t* idx;
+  const float* gate;
+  int h, g, T, R, r;
+  int n_row_tiles;
+  int BG;
+  float c;  // scale * log2(e)
+  int causal, out_bf16, zero_unselected;
+};
+
+// Zero the output rows of heads the router did not keep, for the tokens whose
+// first row lies in this block's row range.
+template <int D>
+__device__ void zero_unselected_rows(const KArgs& a, int b, int gam, int row0, int n_rows) {
+  const int R = a.R, r = a.r;
+  const int t_lo = div_up(row0, R);
+  const int t_hi = (min(row0 + kRowsPerBlock, n_rows) - 1) / R;
+  if (t_hi < t_lo) return;
+  constexpr int CPR = D / 8;
+  const int n_items = (t_hi - t_lo + 1) * r * CPR;
+  for (int c = threadIdx.x; c < n_items; c += kThreads) {
+    const int tt = c / (r * CPR);
+    const int rem = c - tt * r * CPR;
+    const int e = rem / CPR;
+    const int ch = rem - e * CPR;
+    const int t = t_lo + tt;
+    const int head = gam * r + e;
+    const int32_t* sel = a.idx + ((size_t)(b * a.T + t) * a.g + gam) * R;
+    bool kept = false;
+    for (int j = 0; j < R; ++j) kept |= (sel[j] == head);
+    if (kept) continue;
+    const size_t off = ((size_t)(b * a.h + head) * a.T + t) * D + ch * 8;
+    const uint4 z = {0u, 0u, 0u, 0u};
+    if (a.out_bf16) {
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + off) = z;
+    } else {
+      uint4* p = reinterpret_cast<uint4*>(static_cast<float*>(a.out) + off);
+      p[0] = z;
+      p[1] = z;
+    }
+  }
+}
+
+template <int D, bool ROUTED>
+__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
+  using L = Tile<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (L::kElems + L::vElems)];
+  uint16_t* Ks = smem;
+  uint16_t* Vs = smem + 2 * L::kElems;
+
+  const int bid = blockIdx.x;
+  const int bg = bid % a.BG;
+  const int tile = a.causal ? (a.n_row_tiles - 1 - bid / a.BG) : (bid / a.BG);
+  const int b = bg / a.g;
+  const int gam = bg - b * a.g;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hq = lane >> 5;  // which half of the reduction dim / key quad this lane holds
+  const int n_rows = a.T * a.R;
+  const int row0 = tile * kRowsPerBlock;
+
+  if (ROUTED && a.zero_unselected) zero_unselected_rows<D>(a, b, gam, row0, n_rows);
+
+  // This lane's attention row.
+  const int rho = row0 + wave * 32 + l32;
+  const bool row_valid = rho < n_rows;
+  const int rho_c = row_valid ? rho : n_rows - 1;
+  const int t_row = rho_c / a.R;
+  const int slot = rho_c - t_row * a.R;
+  int head;
+  float gate = 1.0f;
+  if (ROUTED) {
+    const size_t o = ((size_t)(b * a.T + t_row) * a.g + gam) * a.R + slot;
+    head = a.idx[o];
+    gate = a.gate[o];
+  } else {
+    head = gam * a.r + slot;
+  }
+
+  // Token range of this wave and of the block (uniform values).
+  const int wrow0 = row0 + wave * 32;
+  const bool wave_has_rows = wrow0 < n_rows;
+  const int wt_lo = min(wrow0, n_rows - 1) / a.R;
+  const int wt_hi = (min(wrow0 + 31, n_rows - 1)) / a.R;
+  const int t_last = (min(row0 + kRowsPerBlock, n_rows) - 1) / a.R;
+  const int n_keys = a.causal ? t_last + 1 : a.T;
+  const int n_tiles = div_up(n_keys, kBN);
+
+  // Q^T fragments: B operand of S^T = K Q^T. Lane half hq holds d in
+  // [hq*D/2, hq*D/2 + D/2); step st uses 8 of them.
+  bf16x8 qf[D / 16];
+  {
+    const uint16_t* qrow = a.q + ((size_t)(b * a.h + head) * a.T + t_row) * D + hq * (D / 2);
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 8 * st);
+  }
+
+  const uint16_t* kbase = a.k + (size_t)bg * a.T * D;
+  const uint16_t* vbase = a.v + (size_t)bg * a.T * D;
+  uint4 rk[L::kLoads], rv[L::kLoads];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < L::kLoads; ++i) {
+      const int c = tid + i * kThreads;
+      const int key = kt * kBN + c / L::kCPR;
+      const int col = (c % L::kCPR) * 8;
+      if (key < a.T) {
+        rk[i] = *reinterpret_cast<const uint4*>(kbase + (size_t)key * D + col);
+        rv[i] = *reinterpret_cast<const uint4*>(vbase + (size_t)key * D + col);
+      } else {
+        rk[i] = make_uint4(0u, 0u, 0u, 0u);  // keys past T: finite zeros, masked below
+        rv[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < L::kLoads; ++i) {
+      const int c = tid + i * kThreads;
+      const int row = c / L::kCPR;
+      const int col = (c % L::kCPR) * 8;
+      *reinterpret_cast<uint4*>(Ks + buf * L::kElems + row * L::kPitch + col) = rk[i];
+      *reinterpret_cast<uint4*>(Vs + buf * L::vElems + row * L::vPitch + col) = rv[i];
+    }
+  };
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+
+  // Lane roles for the transposing V reads.
+  const int grp = lane >> 4;
+  const int i16 = lane & 15;
+  const int tr_row = 4 * hq + (i16 >> 2);
+  const int tr_col = 16 * (grp & 1) + 4 * (i16 & 3);
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_tiles) load_tile(kt + 1);
+    const int key0 = kt * kBN;
+    const bool active = wave_has_rows && (!a.causal || key0 <= wt_hi);
+    if (active) {
+      // S^T[key][row] for the 64 keys of this tile, two 32-key blocks.
+      f32x16 s[2];
+      const uint16_t* kl = Ks + buf * L::kElems;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        const uint16_t* krow = kl + (kb * 32 + l32) * L::kPitch + hq * (D / 2);
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st)
+          s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(krow + 8 * st), qf[st], s[kb]);
+      }
+      // Mask keys past the row's limit: (kb, i) holds key key0 + 32kb + 8(i/4) + 4hq + i%4.
+      const bool need_mask = (a.causal && key0 + kBN - 1 > wt_lo) || (key0 + kBN > a.T);
+      if (need_mask) {
+        const int lim = a.causal ? t_row : a.T - 1;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * hq + (i & 3);
+            if (key > lim) s[kb][i] = -INFINITY;
+          }
+      }
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, s[kb][i]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      const float m_new = fmaxf(m_run, mloc * a.c);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+
+      // P^T as bf16 B operands: step u covers keys 16u .. 16u+15 of the tile.
+      bf16x8 pf[4];
+      float psum = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pv[j] = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + j], a.c, -m_new));
+          psum += pv[j];
+        }
+        pf[u] = pack_bf16x8(pv);
+      }
+      l_run += psum;
+
+      // O^T += V^T P^T. Element j of step u is key 16u + 8(j/4) + 4hq + j%4,
+      // which the two transposing reads fetch for d = 32db + l%32.
+      const uint16_t* vl = Vs + buf * L::vElems;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint16_t* p0 = vl + (16 * u + tr_row) * L::vPitch + tr_col;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const bf16x8 vf = lds_read_tr_pair(p0 + 32 * db, p0 + 8 * L::vPitch + 32 * db);
+          o[db] = mfma32x32x16(vf, pf[u], o[db]);
+        }
+      }
+    }
+    if (kt + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (row_valid) {
+    const float inv = gate / l_tot;
+    const size_t obase = ((size_t)(b * a.h + head) * a.T + t_row) * D + 4 * hq;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const size_t off = obase + 32 * db + 8 * i4;
+        const float x0 = o[db][4 * i4 + 0] * inv, x1 = o[db][4 * i4 + 1] * inv;
+        const float x2 = o[db][4 * i4 + 2] * inv, x3 = o[db][4 * i4 + 3] * inv;
+        if (a.out_bf16) {
+          uint2 w = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) = w;
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + off) = make_float4(x0, x1, x2, x3);
+        }
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
+  KArgs a;
+  a.q = static_cast<const uint16_t*>(p.q);
+  a.k = static_cast<const uint16_t*>(p.k);
+  a.v = static_cast<const uint16_t*>(p.v);
+  a.out = p.out;
+  a.idx = p.idx;
+  a.gate = p.gate;
+  a.h = p.h;
+  a.g = p.g;
+  a.T = p.T;
+  a.R = p.R;
+  a.r = p.h / p.g;
+  a.n_row_tiles = div_up(p.T * p.R, kRowsPerBlock);
+  a.BG = p.B * p.g;
+  a.c = p.scale * kLog2e;
+  a.causal = p.causal;
+  a.out_bf16 = p.out_bf16;
+  a.zero_unselected = p.zero_unselected;
+  const dim3 grid(a.n_row_tiles * a.BG), block(kThreads);
+  if (p.idx)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_bf16_supports(int d) { return d == 64 || d == 128; }
+
+hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
+  switch (p.d) {
+    case 64: return launch_d<64>(p, stream);
+    case 128: return launch_d<128>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gqa

@@ -1,0 +1,67 @@
+// Host-side launch interface between the C ABI (api.hip) and the kernels.
+// Every function here enqueues work on `stream` and returns the launch status;
+// arguments have already been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gqa {
+
+// One attention row is one (token, query head) pair of one (batch, KV group).
+// Rows are ordered token-major: row rho of group (b, gamma) is token rho / R,
+// slot rho % R. Dense GQA uses R = h/g and slot j is head gamma*(h/g) + j.
+// Routed GQE uses R = top_k and slot j is head idx[b, t, gamma, j], with the
+// output row multiplied by gate[b, t, gamma, j].
+struct AttnParams {
+  const void* q;        // [B, h, T, d]
+  const void* k;        // [B, g, T, d]
+  const void* v;        // [B, g, T, d]
+  void* out;            // [B, h, T, d]
+  const int32_t* idx;   // routed only: [B, T, g, R] global head ids, else null
+  const float* gate;    // routed only: [B, T, g, R], else null
+  int B, h, g, T, d;
+  int R;                // rows per token
+  float scale;          // > 0
+  int causal;           // 0 or 1
+  int out_bf16;         // 1: bf16 output, 0: fp32 output
+  int zero_unselected;  // routed only: write zeros to the rows of unselected heads
+};
+
+struct RouterParams {
+  const float* logits;  // [B, T, h]
+  int32_t* idx;         // [B, T, g, k]
+  float* gate;          // [B, T, g, k]
+  int B, T, h, g, k;
+};
+
+struct DecodeParams {
+  const void* q;        // [B, h, d] bf16
+  const void* k_cache;  // [B, g, T_max, d] bf16
+  const void* v_cache;  // [B, g, T_max, d] bf16
+  const int32_t* lens;  // [B] on the device
+  void* out;            // [B, h, d]
+  float* part_acc;      // [B*h, n_split, d] fp32 workspace
+  float* part_ml;       // [B*h, n_split, 2] fp32 workspace
+  int B, h, g, T_max, d;
+  int chunk;            // keys per split (multiple of 128)
+  int n_split;          // ceil(T_max / chunk)
+  float scale;
+  int out_bf16;
+};
+
+hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
+hipError_t launch_router(const RouterParams& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+// Head dims with a bf16 MFMA prefill kernel / an fp32 kernel / a decode kernel.
+bool attn_bf16_supports(int d);
+bool attn_f32_supports(int d);
+bool decode_supports(int d);
+
+// Decode split size in keys for a problem shape (honours GQA_DECODE_CHUNK).
+int decode_chunk(int B, int h, int g, int T_max);
+
+}  // namespace gqa

@@ -1,0 +1,153 @@
+/*
+ * libgqa -- grouped-query attention (GQA) and grouped query experts (GQE)
+ * for AMD Instinct MI355X (gfx950). C ABI.
+ *
+ * Problem statement the entry points follow:
+ *  - GQA (ml-canon "56 GQA / MQA", section "Idea and mechanism" and the
+ *    PyTorch GQA function; IBM Think "What is grouped query attention
+ *    (GQA)?"): h query heads are split into g groups and every group shares
+ *    one key/value head; g = 1 is multi-query attention (MQA), g = h is
+ *    multi-head attention (MHA). q is [B, h, T, d], k and v are [B, g, T, d],
+ *    g divides h, query head i reads KV head i / (h/g) (contiguous groups:
+ *    freenetmedia "Grouped-Query Attention", section on how it works, example
+ *    of 8 heads in 2 groups).
+ *  - Attention per head (IBM Think page, scaled dot-product attention):
+ *    out = softmax(q k^T * scale) v over keys, scale usually 1/sqrt(d).
+ *  - Causal mask: query at position t sees keys 0..t (IBM Think page, on
+ *    autoregressive decoders attending to previous tokens).
+ *  - Decode over a KV cache (aiunderstanding.org "Attention aux requetes
+ *    groupees", section "Plongee profonde"): the keys and values of all
+ *    previous tokens are cached, and one new query per sequence attends to
+ *    them.
+ *  - GQE (gist.science explainer of "Grouped Query Experts: Mixture-of-Experts
+ *    on GQA Self-Attention", section "Architecture et Routage"): a router keeps
+ *    k query-head experts per token inside every KV group; K/V stay dense; the
+ *    kept outputs are weighted by router probabilities renormalised over the
+ *    k kept.
+ *
+ * Conventions for every entry point:
+ *  - Memory: all tensor pointers are device pointers to caller-owned memory,
+ *    contiguous row-major in the stated layouts, 16-byte aligned. The library
+ *    allocates nothing and frees nothing; it keeps no state between calls
+ *    except a thread-local error message.
+ *  - dtypes: GQA_F32 = IEEE fp32, GQA_BF16 = bfloat16 (raw 16-bit storage).
+ *    Accumulation is always fp32; fp32 inputs are never rounded to bf16.
+ *  - Execution: work is enqueued on `stream` (a hipStream_t, NULL = the
+ *    default stream) and the call returns without synchronising. A fault in
+ *    a kernel surfaces at the caller's next synchronisation.
+ *  - Errors: arguments are checked before any HIP call; a rejected call
+ *    returns GQA_ERR_INVALID_ARG or GQA_ERR_UNSUPPORTED and enqueues nothing.
+ *    GQA_ERR_NO_DEVICE means no HIP device is visible. GQA_ERR_HIP means a
+ *    HIP launch failed. gqa_last_error() returns the calling thread's
+ *    message for its last failed call.
+ *  - Empty problems (B = 0 or T = 0) return GQA_OK and enqueue nothing.
+ *  - scale must be finite and > 0. causal must be 0 or 1.
+ *  - Element counts must fit the int32 index arithmetic of the kernels:
+ *    h*T and g*T below 2^31 per batch element (byte offsets are 64-bit).
+ */
+#ifndef GQA_H_
+#define GQA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARG = 1,
+  GQA_ERR_UNSUPPORTED = 2,
+  GQA_ERR_WORKSPACE = 3,
+  GQA_ERR_NO_DEVICE = 4,
+  GQA_ERR_HIP = 5
+} gqa_status;
+
+typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
+
+/* Version of this ABI; bumped on any incompatible change. */
+int gqa_abi_version(void);
+
+/*
+ * GQA prefill (self-attention over one sequence block).
+ *   q   [B, h, T, d] in_dtype      k, v [B, g, T, d] in_dtype
+ *   out [B, h, T, d] out_dtype (written in full)
+ * out[b, i, t] = sum_j softmax_j(scale * q[b,i,t] . k[b, i/(h/g), j]) v[b, i/(h/g), j]
+ * over j <= t when causal, over all j < T otherwise.
+ * Supported: in_dtype BF16 with d in {64, 128}; in_dtype F32 with
+ * d in {16, 32, 64, 128}; out_dtype F32 or BF16 (round to nearest even).
+ */
+gqa_status gqa_prefill(const void* q, const void* k, const void* v, void* out,
+                       int B, int h, int g, int T, int d,
+                       gqa_dtype in_dtype, gqa_dtype out_dtype,
+                       float scale, int causal, void* stream);
+
+/*
+ * Bytes of device workspace gqa_decode needs for this shape (0 when the
+ * cache fits one split). Depends only on the arguments (and on the
+ * GQA_DECODE_CHUNK environment variable, which overrides the split size).
+ */
+size_t gqa_decode_workspace_bytes(int B, int h, int g, int T_max, int d);
+
+/*
+ * GQA decode: one new query token per sequence over a KV cache.
+ *   q       [B, h, d] in_dtype
+ *   k_cache [B, g, T_max, d] in_dtype, v_cache the same
+ *   lens    [B] int32, device memory: valid cached positions per sequence,
+ *           read on the device and clamped to [0, T_max]. The cache already
+ *           holds the new token's key/value at position lens[b]-1. Positions
+ *           >= lens[b] are never read (they may hold anything, NaN included).
+ *   out     [B, h, d] out_dtype; lens[b] = 0 gives a zero row.
+ *   workspace: device memory of at least gqa_decode_workspace_bytes(...)
+ *           bytes (may be NULL when that is 0); contents are scratch.
+ * Supported: in_dtype BF16, d in {64, 128}, h/g <= 64.
+ * Returns GQA_ERR_WORKSPACE when workspace_bytes is too small.
+ */
+gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* lens, void* out,
+                      int B, int h, int g, int T_max, int d,
+                      gqa_dtype in_dtype, gqa_dtype out_dtype, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * GQE routed prefill.
+ *   q [B, h, T, d], k/v [B, g, T, d] in_dtype, as for gqa_prefill.
+ *   router_logits [B, T, h] fp32, device: the router's score of every query
+ *           head (expert) for every token.
+ *   top_k   experts kept per (token, group), 1 <= top_k <= h/g <= 64.
+ *   topk_idx  [B, T, g, top_k] int32, written: global head ids of the kept
+ *           experts in rank order (higher logit first, equal logits by lower
+ *           head id).
+ *   topk_gate [B, T, g, top_k] fp32, written: softmax of the kept logits
+ *           (router probabilities renormalised over the kept experts).
+ *   out [B, h, T, d] out_dtype, written in full: out[b, i, t] is
+ *           gate * (GQA attention row of head i at token t, dense K/V) when
+ *           the router kept head i for token t, and 0 otherwise.
+ * Supported: as gqa_prefill.
+ */
+gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v,
+                              const float* router_logits, int top_k,
+                              void* out, int32_t* topk_idx, float* topk_gate,
+                              int B, int h, int g, int T, int d,
+                              gqa_dtype in_dtype, gqa_dtype out_dtype,
+                              float scale, int causal, void* stream);
+
+/*
+ * KV-cache size in bytes for one layer: 2 (keys and values) * n_kv * d * T
+ * * sizeof(dtype) * B (ml-canon page, section on where the KV-cache saving
+ * comes from). Returns 0 for negative sizes.
+ */
+uint64_t gqa_kv_cache_bytes(int B, int n_kv, int T, int d, gqa_dtype dtype);
+
+/* Static description of a status code. */
+const char* gqa_status_string(gqa_status status);
+
+/* Detail message of the calling thread's last failed call ("" if none). */
+const char* gqa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H_ */

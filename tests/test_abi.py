@@ -1,0 +1,146 @@
+"""The C-ABI library without a GPU: it loads, exports every function the
+header declares, rejects bad arguments before touching HIP, and answers the
+size queries. No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import gqa_routed_query_amd as gq
+from gqa_routed_query_amd import _binding
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, NO_DEVICE = 0, 1, 2, 3, 4
+F32, BF16 = gq.GQA_F32, gq.GQA_BF16
+P = 0x100000  # an aligned, never dereferenced stand-in pointer
+lib = _binding._lib
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:gqa|gqe)_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = _declared_functions()
+    assert {"gqa_prefill", "gqa_decode", "gqe_routed_prefill"} <= set(names)
+    so = ctypes.CDLL(gq.lib_path)
+    for n in names:
+        assert hasattr(so, n), f"{n} declared in gqa.h but not exported"
+
+
+def test_abi_version_and_status_strings():
+    assert gq.abi_version() == 1
+    for s in range(6):
+        assert gq.status_string(s)
+    assert gq.status_string(99) == "unknown status"
+
+
+def _prefill(**kw):
+    a = dict(q=P, k=P, v=P, out=P, B=1, h=4, g=2, T=16, d=16, i=F32, o=F32, scale=0.25,
+             causal=1, stream=None)
+    a.update(kw)
+    return lib.gqa_prefill(a["q"], a["k"], a["v"], a["out"], a["B"], a["h"], a["g"], a["T"],
+                           a["d"], a["i"], a["o"], a["scale"], a["causal"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h=6, g=4), INVALID),            # g does not divide h
+    (dict(g=0), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(T=-3), INVALID),
+    (dict(scale=0.0), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(scale=-1.0), INVALID),
+    (dict(causal=2), INVALID),
+    (dict(q=None), INVALID),
+    (dict(out=P + 4), INVALID),            # misaligned
+    (dict(i=7), INVALID),                  # unknown dtype
+    (dict(d=48), UNSUPPORTED),
+    (dict(i=BF16, d=16), UNSUPPORTED),
+    (dict(h=1 << 20, g=1, T=1 << 12), INVALID),  # h*T beyond the row limit
+])
+def test_prefill_rejects(kw, status):
+    assert _prefill(**kw) == status
+    assert gq.last_error()
+
+
+def test_prefill_empty_is_ok():
+    assert _prefill(B=0) == OK
+    assert _prefill(T=0, q=None) == OK
+
+
+def _decode(**kw):
+    a = dict(q=P, kc=P, vc=P, lens=P, out=P, B=2, h=8, g=2, T=1024, d=128, i=BF16, o=BF16,
+             scale=0.088, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.gqa_decode(a["q"], a["kc"], a["vc"], a["lens"], a["out"], a["B"], a["h"], a["g"],
+                          a["T"], a["d"], a["i"], a["o"], a["scale"], a["ws"], a["wsb"],
+                          a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h=8, g=3), INVALID),
+    (dict(lens=None), INVALID),
+    (dict(i=F32), UNSUPPORTED),
+    (dict(d=32), UNSUPPORTED),
+    (dict(h=128, g=1), UNSUPPORTED),       # 128 heads per group
+    (dict(wsb=0, T=1 << 16), WORKSPACE),
+    (dict(scale=float("inf")), INVALID),
+])
+def test_decode_rejects(kw, status):
+    assert _decode(**kw) == status
+
+
+def _gqe(**kw):
+    a = dict(q=P, k=P, v=P, lg=P, k_top=1, out=P, idx=P, gate=P, B=1, h=8, g=2, T=16, d=128,
+             i=BF16, o=BF16, scale=0.088, causal=1, stream=None)
+    a.update(kw)
+    return lib.gqe_routed_prefill(a["q"], a["k"], a["v"], a["lg"], a["k_top"], a["out"],
+                                  a["idx"], a["gate"], a["B"], a["h"], a["g"], a["T"], a["d"],
+                                  a["i"], a["o"], a["scale"], a["causal"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_top=0), INVALID),
+    (dict(k_top=5), INVALID),              # more than h/g = 4
+    (dict(lg=None), INVALID),
+    (dict(idx=None), INVALID),
+    (dict(h=130, g=1, k_top=1), UNSUPPORTED),
+])
+def test_gqe_rejects(kw, status):
+    assert _gqe(**kw) == status
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible: would launch")
+def test_valid_calls_report_no_device():
+    assert _prefill() == NO_DEVICE
+    assert _decode() == NO_DEVICE
+    assert _gqe() == NO_DEVICE
+
+
+def test_kv_cache_bytes_matches_oracle_law():
+    for (B, n_kv, T, d) in [(1, 8, 4096, 128), (32, 1, 16384, 128), (64, 8, 4608, 128), (3, 5, 7, 16)]:
+        assert gq.gqa_kv_cache_bytes(B, n_kv, T, d, torch.bfloat16) == \
+            oracle.kv_cache_bytes(B, n_kv, T, d, 2)
+        assert gq.gqa_kv_cache_bytes(B, n_kv, T, d, torch.float32) == \
+            oracle.kv_cache_bytes(B, n_kv, T, d, 4)
+    # the h/g reduction: 32 query heads over 8 KV groups -> 4x smaller cache
+    assert gq.gqa_kv_cache_bytes(1, 32, 4096, 128) == 4 * gq.gqa_kv_cache_bytes(1, 8, 4096, 128)
+
+
+def test_decode_workspace_bytes():
+    assert gq.gqa_decode_workspace_bytes(0, 8, 2, 100, 128) == 0
+    # one split: no workspace
+    assert gq.gqa_decode_workspace_bytes(1, 8, 2, 100, 128) == 0
+    big = gq.gqa_decode_workspace_bytes(64, 32, 8, 8192, 128)
+    assert big > 0
+    # partials are a small fraction of the cache they summarise
+    assert big < 0.05 * gq.gqa_kv_cache_bytes(64, 8, 8192, 128)

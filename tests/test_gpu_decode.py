@@ -1,0 +1,132 @@
+"""GQA decode over a KV cache on the GPU against the float64 oracle."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL_BF16, dev, max_abs, np64, say
+from workloads import WORKLOADS, decode_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(q, kc, vc, lens, out_dtype=torch.float32):
+    import gqa_routed_query_amd as gq
+
+    d = dev()
+    out = gq.gqa_decode(q.to(d), kc.to(d), vc.to(d), lens.to(d), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("B,h,g,T_max,d,out_dt", [
+    (5, 8, 2, 1000, 128, torch.float32),
+    (5, 8, 2, 1000, 128, torch.bfloat16),
+    (3, 32, 1, 700, 128, torch.float32),     # MQA: 32 heads on one KV head
+    (3, 16, 16, 300, 128, torch.float32),    # MHA
+    (4, 16, 2, 400, 64, torch.float32),      # d = 64
+    (2, 64, 1, 130, 128, torch.float32),     # 64 heads per group
+])
+def test_decode_shapes_poisoned_padding(B, h, g, T_max, d, out_dt):
+    say(f"decode B={B} h={h} g={g} T_max={T_max} d={d} out={out_dt}")
+    q, kc, vc, lens = decode_inputs(B, h, g, T_max, d, (1, T_max), seed=300 + h,
+                                    poison_padding=True)
+    lens[0] = T_max
+    lens[-1] = 1
+    kc[0] = kc[0].nan_to_num(0.0)  # row 0 is full: no padding there
+    vc[0] = vc[0].nan_to_num(0.0)
+    out = _run(q, kc, vc, lens, out_dt)
+    assert torch.isfinite(out).all()
+    err = max_abs(out, oracle.gqa_decode_ref(q, kc, vc, lens))
+    assert err <= TOL_BF16, err
+
+
+def test_decode_edge_lengths():
+    """Lengths around the 32-key sub-block and 128-key chunk boundaries, plus
+    an empty sequence (zero row)."""
+    lens_list = [0, 1, 31, 32, 33, 127, 128, 129, 255, 256, 511, 512]
+    B = len(lens_list)
+    say("decode edge lengths")
+    q, kc, vc, _ = decode_inputs(B, 8, 2, 512, 128, (1, 1), seed=31, poison_padding=False)
+    lens = torch.tensor(lens_list, dtype=torch.int32)
+    for b, n in enumerate(lens_list):
+        kc[b, :, n:] = float("nan")
+        vc[b, :, n:] = float("nan")
+    out = _run(q, kc, vc, lens)
+    ref = oracle.gqa_decode_ref(q, kc, vc, lens)
+    assert torch.isfinite(out).all()
+    assert float(out[0].abs().max()) == 0.0
+    assert max_abs(out, ref) <= TOL_BF16
+
+
+def test_decode_split_invariance(monkeypatch):
+    """The result does not depend on the split size (up to fp32 rounding)."""
+    q, kc, vc, lens = decode_inputs(4, 16, 4, 3000, 128, (1, 3000), seed=41)
+    outs = []
+    for chunk in ("128", "512", "4096"):
+        say(f"decode split chunk={chunk}")
+        monkeypatch.setenv("GQA_DECODE_CHUNK", chunk)
+        outs.append(_run(q, kc, vc, lens))
+    monkeypatch.delenv("GQA_DECODE_CHUNK")
+    assert max_abs(outs[0], outs[1]) <= 1e-3
+    assert max_abs(outs[0], outs[2]) <= 1e-3
+    assert max_abs(outs[0], oracle.gqa_decode_ref(q, kc, vc, lens)) <= TOL_BF16
+
+
+def test_decode_matches_prefill_last_row():
+    """Decoding token t over a cache of t+1 positions equals row t of causal
+    prefill (both on the GPU, both checked against the oracle)."""
+    import gqa_routed_query_amd as gq
+    from workloads import prefill_inputs
+
+    d = dev()
+    say("decode vs prefill row")
+    q, k, v = prefill_inputs(1, 8, 2, 200, 128, "bf16", seed=51)
+    pre = gq.gqa_prefill(q.to(d), k.to(d), v.to(d), causal=True, out_dtype=torch.float32)
+    ts = [0, 63, 64, 199]
+    qd = torch.stack([q[0, :, t] for t in ts])
+    kc = k.expand(len(ts), -1, -1, -1).contiguous()
+    vc = v.expand(len(ts), -1, -1, -1).contiguous()
+    lens = torch.tensor([t + 1 for t in ts], dtype=torch.int32)
+    out = _run(qd, kc, vc, lens)
+    for j, t in enumerate(ts):
+        assert max_abs(out[j], pre[0, :, t]) <= 5e-3
+
+
+def test_decode_headline_shape():
+    """B=64, h=32, g=8, d=128, cache lengths uniform in [1024, 8192], cache
+    drawn on the GPU (seed 3); 8 sequences checked in full against the oracle,
+    the rest for finiteness."""
+    w = WORKLOADS["decode"]
+    d = dev()
+    say("decode headline shape")
+    q, kc, vc, lens = decode_inputs(w.B, w.h, w.g, w.T, w.d, w.lens, seed=w.seed, device=d)
+    out = _run(q, kc, vc, lens)
+    assert torch.isfinite(out).all()
+    lens_c = lens.cpu()
+    picks = sorted({int(lens_c.argmin()), int(lens_c.argmax()), 0, 1, 17, 33, 50, 63})
+    for b in picks:
+        n = int(lens_c[b])
+        ref = oracle.gqa_decode_ref(q[b:b + 1].cpu(), kc[b:b + 1, :, :n].cpu(),
+                                    vc[b:b + 1, :, :n].cpu(), np.array([n]))
+        assert max_abs(out[b:b + 1], ref) <= TOL_BF16, b
+
+
+@pytest.mark.parametrize("g", WORKLOADS["decode_sweep"].g_sweep)
+def test_decode_group_sweep(g):
+    """B=32, h=32, T=16384, d=128 at g in {1, 4, 8, 32}: two sequences checked
+    in full against the oracle, every output finite."""
+    w = WORKLOADS["decode_sweep"]
+    d = dev()
+    say(f"decode sweep g={g}")
+    q, kc, vc, lens = decode_inputs(w.B, w.h, g, w.T, w.d, w.lens, seed=w.seed + g, device=d)
+    out = _run(q, kc, vc, lens)
+    assert torch.isfinite(out).all()
+    for b in (0, w.B - 1):
+        ref = oracle.gqa_decode_ref(q[b:b + 1].cpu(), kc[b:b + 1].cpu(), vc[b:b + 1].cpu(),
+                                    np.array([w.T]))
+        assert max_abs(out[b:b + 1], ref) <= TOL_BF16, b
+    del q, kc, vc
+    torch.cuda.empty_cache()

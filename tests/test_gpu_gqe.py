@@ -1,0 +1,92 @@
+"""GQE routed prefill on the GPU against the float64 oracle: router indices
+bit-exact, gates within 1e-6, outputs within the dtype tolerance, unselected
+rows exactly zero."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL_BF16, TOL_F32, TOL_GATE, dev, max_abs, np64, sample_tokens, say
+from workloads import WORKLOADS, gqe_inputs, prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(q, k, v, lg, top_k, causal=True, out_dtype=torch.float32):
+    import gqa_routed_query_amd as gq
+
+    d = dev()
+    res = gq.gqe_routed_prefill(q.to(d), k.to(d), v.to(d), lg.to(d), top_k, causal=causal,
+                                out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return res
+
+
+@pytest.mark.parametrize("B,h,g,T,d,top_k,ties,dt", [
+    (2, 8, 2, 300, 128, 1, False, "bf16"),
+    (2, 8, 2, 300, 128, 2, False, "bf16"),
+    (1, 8, 2, 300, 128, 4, False, "bf16"),   # all experts kept: gated dense
+    (2, 8, 2, 129, 128, 2, True, "bf16"),    # many tied logits
+    (1, 12, 4, 100, 64, 3, True, "bf16"),
+    (1, 32, 1, 80, 128, 5, False, "bf16"),   # one group of 32 experts
+    (1, 4, 2, 40, 16, 1, False, "f32"),
+    (1, 8, 2, 70, 32, 2, True, "f32"),
+])
+def test_gqe_shapes(B, h, g, T, d, top_k, ties, dt):
+    say(f"gqe B={B} h={h} g={g} T={T} d={d} k={top_k} ties={ties} {dt}")
+    q, k, v, lg = gqe_inputs(B, h, g, T, d, dt, seed=400 + T + top_k, ties=ties)
+    out, idx, gate = _run(q, k, v, lg, top_k)
+    ref, ridx, rgate = oracle.gqe_ref(q, k, v, lg, top_k, causal=True)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert max_abs(gate, rgate) <= TOL_GATE
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    assert max_abs(out, ref) <= tol
+    # a row is nonzero iff the router kept its head for its token
+    assert torch.equal((out.cpu() != 0).any(-1), torch.from_numpy((ref != 0).any(-1)))
+
+
+def test_gqe_top1_rows_equal_dense_rows():
+    """With k = 1 the gate is 1 and a kept row is the dense GQA row."""
+    import gqa_routed_query_amd as gq
+
+    d = dev()
+    say("gqe k=1 vs dense prefill")
+    q, k, v, lg = gqe_inputs(1, 8, 2, 260, 128, "bf16", seed=61)
+    out, idx, gate = _run(q, k, v, lg, 1)
+    dense = gq.gqa_prefill(q.to(d), k.to(d), v.to(d), causal=True, out_dtype=torch.float32)
+    assert bool((gate == 1.0).all())
+    idx_c = idx.cpu()
+    for t in range(0, 260, 7):
+        for gam in range(2):
+            i = int(idx_c[0, t, gam, 0])
+            assert max_abs(out[0, i, t], dense[0, i, t]) <= 1e-6
+
+
+@pytest.mark.parametrize("top_k", WORKLOADS["gqe"].top_k)
+def test_gqe_headline_shape(top_k):
+    """B=2, T=4096, h=32, g=8, d=128, logits N(0,1) (seed 5), drawn on the GPU:
+    all router indices bit-exact and gates checked; sampled rows against the
+    oracle; every unselected row exactly zero."""
+    w = WORKLOADS["gqe"]
+    d = dev()
+    say(f"gqe headline shape k={top_k}")
+    q, k, v, lg = gqe_inputs(w.B, w.h, w.g, w.T, w.d, "bf16", seed=w.seed, device=d)
+    out, idx, gate = _run(q, k, v, lg, top_k, out_dtype=torch.bfloat16)
+    ridx, rgate = oracle.gqe_topk_ref(lg.cpu(), w.g, top_k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert max_abs(gate, rgate) <= TOL_GATE
+    # structure: a row is nonzero iff its head was kept for its token
+    kept = torch.zeros(w.B, w.T, w.h, dtype=torch.bool)
+    kept.scatter_(2, torch.from_numpy(ridx.reshape(w.B, w.T, -1)).long(), True)
+    nz = (out != 0).any(-1).cpu().permute(0, 2, 1)  # [B,T,h]
+    assert torch.equal(nz, kept)
+    qc, kc, vc, oc = q.cpu(), k.cpu(), v.cpu(), out.cpu()
+    worst = 0.0
+    for t in sample_tokens(w.T, 40, seed=3):
+        for b in range(w.B):
+            for gam in (0, w.g - 1):
+                for j in range(top_k):
+                    i = int(ridx[b, t, gam, j])
+                    ref = rgate[b, t, gam, j] * oracle.gqa_ref_row(qc, kc, vc, b, i, t)
+                    worst = max(worst, float(np.abs(np64(oc[b, i, t]) - ref).max()))
+    assert worst <= TOL_BF16, worst

@@ -1,0 +1,128 @@
+"""GQA prefill on the GPU against the float64 oracle, element by element."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL_BF16, TOL_F32, dev, max_abs, np64, sample_tokens, say
+from workloads import WORKLOADS, prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(q, k, v, causal=True, out_dtype=None, scale=None):
+    import gqa_routed_query_amd as gq
+
+    d = dev()
+    out = gq.gqa_prefill(q.to(d), k.to(d), v.to(d), causal=causal, out_dtype=out_dtype,
+                         scale=scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_tiny_fp32_gqa_mha_mqa():
+    """B=1, h=4, T=16, d=16 fp32, causal, at g=2 (GQA), g=4 (MHA), g=1 (MQA):
+    one draw, the same q and the first g KV heads."""
+    w = WORKLOADS["tiny_f32"]
+    q, k4, v4 = prefill_inputs(w.B, w.h, 4, w.T, w.d, "f32", seed=w.seed)
+    for g in w.g_sweep:
+        k, v = k4[:, :g].contiguous(), v4[:, :g].contiguous()
+        say(f"tiny fp32 g={g}")
+        out = _run(q, k, v, causal=True)
+        err = max_abs(out, oracle.gqa_ref(q, k, v, causal=True))
+        assert err <= TOL_F32, (g, err)
+
+
+@pytest.mark.parametrize("B,h,g,T,d,causal", [
+    (1, 4, 2, 1, 16, True),        # T = 1: output is V
+    (2, 8, 2, 77, 16, True),
+    (1, 6, 3, 130, 32, False),
+    (2, 4, 1, 97, 64, True),       # MQA
+    (1, 4, 4, 300, 128, True),     # MHA, several tiles, ragged tail
+    (1, 8, 2, 259, 128, False),
+])
+def test_fp32_shapes(B, h, g, T, d, causal):
+    say(f"fp32 B={B} h={h} g={g} T={T} d={d} causal={causal}")
+    q, k, v = prefill_inputs(B, h, g, T, d, "f32", seed=100 + T)
+    out = _run(q, k, v, causal=causal)
+    err = max_abs(out, oracle.gqa_ref(q, k, v, causal=causal))
+    assert err <= TOL_F32, err
+
+
+@pytest.mark.parametrize("B,h,g,T,d,causal,out_dt", [
+    (1, 4, 2, 1, 128, True, torch.float32),        # T = 1
+    (2, 8, 2, 300, 128, True, torch.float32),      # several row and key tiles, ragged tail
+    (2, 8, 2, 300, 128, True, torch.bfloat16),
+    (1, 8, 2, 300, 128, False, torch.float32),
+    (1, 4, 4, 130, 128, True, torch.float32),      # MHA
+    (1, 8, 1, 257, 128, True, torch.float32),      # MQA
+    (1, 32, 8, 520, 128, True, torch.bfloat16),    # the headline head layout
+    (2, 6, 3, 190, 64, True, torch.float32),       # d = 64
+    (1, 12, 4, 333, 64, False, torch.bfloat16),
+    (1, 2, 1, 64, 128, True, torch.float32),       # exactly one tile
+    (1, 4, 2, 65, 128, True, torch.float32),       # one tile plus one key
+])
+def test_bf16_shapes(B, h, g, T, d, causal, out_dt):
+    say(f"bf16 B={B} h={h} g={g} T={T} d={d} causal={causal} out={out_dt}")
+    q, k, v = prefill_inputs(B, h, g, T, d, "bf16", seed=200 + T + h)
+    out = _run(q, k, v, causal=causal, out_dtype=out_dt)
+    err = max_abs(out, oracle.gqa_ref(q, k, v, causal=causal))
+    assert err <= TOL_BF16, err
+
+
+def test_bf16_explicit_scale():
+    say("bf16 explicit scale 0.3")
+    q, k, v = prefill_inputs(1, 8, 2, 150, 128, "bf16", seed=7)
+    out = _run(q, k, v, causal=True, out_dtype=torch.float32, scale=0.03)
+    err = max_abs(out, oracle.gqa_ref(q, k, v, causal=True, scale=0.03))
+    assert err <= TOL_BF16, err
+
+
+def test_bf16_headline_shape_sampled_rows():
+    """B=4, h=32, g=8, T=2048, d=128, causal, inputs drawn on the GPU (seed 2);
+    edge and random rows checked one by one against the oracle."""
+    w = WORKLOADS["prefill"]
+    d = dev()
+    say("prefill headline shape, sampled rows")
+    q, k, v = prefill_inputs(w.B, w.h, w.g, w.T, w.d, "bf16", seed=w.seed, device=d)
+    out = _run(q, k, v, causal=True)
+    qc, kc, vc, oc = q.cpu(), k.cpu(), v.cpu(), out.cpu()
+    rng = np.random.default_rng(0)
+    worst = 0.0
+    for t in sample_tokens(w.T, 48, seed=1):
+        b = int(rng.integers(0, w.B))
+        for i in (0, int(rng.integers(0, w.h)), w.h - 1):
+            ref = oracle.gqa_ref_row(qc, kc, vc, b, i, t, causal=True)
+            worst = max(worst, float(np.abs(np64(oc[b, i, t]) - ref).max()))
+    assert worst <= TOL_BF16, worst
+
+
+def test_bf16_headline_shape_unit_values():
+    """At the headline shape with V = 1 everywhere every output is 1 (the
+    weights of a row sum to one), whatever q and k are."""
+    w = WORKLOADS["prefill"]
+    d = dev()
+    say("prefill headline shape, V = 1")
+    q, k, _ = prefill_inputs(w.B, w.h, w.g, w.T, w.d, "bf16", seed=w.seed, device=d)
+    v = torch.ones_like(k)
+    out = _run(q, k, v, causal=True, out_dtype=torch.float32)
+    assert float((out - 1.0).abs().max()) <= TOL_BF16
+
+
+def test_bf16_deterministic():
+    say("bf16 determinism")
+    q, k, v = prefill_inputs(2, 8, 2, 300, 128, "bf16", seed=9)
+    a = _run(q, k, v, causal=True)
+    b = _run(q, k, v, causal=True)
+    assert torch.equal(a, b)
+
+
+def test_empty_problem():
+    import gqa_routed_query_amd as gq
+
+    d = dev()
+    say("empty T = 0")
+    q = torch.empty(1, 4, 0, 128, dtype=torch.bfloat16, device=d)
+    k = torch.empty(1, 2, 0, 128, dtype=torch.bfloat16, device=d)
+    out = gq.gqa_prefill(q, k, k, causal=True)
+    assert out.shape == q.shape
