@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the GQA / GQE hot path on one MI355X.
+
+One step runs the whole path once on resident synthetic inputs:
+  * GQA causal prefill, bf16 in / fp32 accumulate: B=4, h=32, g=8, T=2048,
+    d=128 (the headline workload: ``value`` is its TFLOP/s);
+  * GQA decode over a bf16 KV cache: B=64, h=32, g=8, d=128, cache lengths
+    uniform in [1024, 8192] (KV GB/s);
+  * GQE routed causal prefill, bf16: B=2, T=4096, h=32, g=8, d=128, top-k 1
+    and 2 (TFLOP/s of the kept rows).
+Every kernel call is bracketed by HIP events recorded on the stream the
+library launches on (torch's current stream). Before each decode call a
+1 GiB buffer is overwritten (outside the events) so the 256 MB Infinity Cache
+holds none of the KV cache. Work is counted algorithmically: causal prefill
+flops are 4*d per visible (query, key) pair, GQE flops only for kept rows,
+decode bytes only for cached positions below lens[b] (plus q and out).
+
+After the timed steps, the KV-group sweep (decode, B=32, T=16384, g in
+{1, 4, 8, 32}) is timed the same way, and the float64 CPU oracle is timed on
+a bounded sample of the prefill workload (cpu_baseline).
+
+Prints ONE JSON line. Only one GPU is supported.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GQA prefill TFLOP/s + decode KV GB/s (fraction of MI355X peak), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = {
+    "prefill": "gqa_routed_query_amd/csrc/attn_bf16.hip",
+    "decode": "gqa_routed_query_amd/csrc/decode.hip",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the KV-group decode sweep")
+    ap.add_argument("--only", choices=["prefill", "decode", "gqe", "copy"], default=None,
+                    help="profile helper: run only one kernel family (copy = calibration copy)")
+    return ap.parse_args()
+
+
+def source_hash(rel):
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(name, n_launch_units=1):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[name]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[name]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Timer:
+    """Per-call HIP event pairs on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __enter__(self):
+        self.s = self.torch.cuda.Event(enable_timing=True)
+        self.e = self.torch.cuda.Event(enable_timing=True)
+        self.s.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.e.record()
+        self.pairs.append((self.s, self.e))
+
+    def ms(self):
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gqa_routed_query_amd as gq
+    from workloads import WORKLOADS, decode_inputs, gqe_inputs, prefill_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"device {torch.cuda.get_device_name(dev)}, lib {gq.lib_path}")
+
+    wp, wd, wg = WORKLOADS["prefill"], WORKLOADS["decode"], WORKLOADS["gqe"]
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    if args.only == "copy":
+        # calibration for the HBM byte counters: one 1 GiB device copy
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of 1 GiB")
+        return
+
+    run_prefill = args.only in (None, "prefill")
+    run_decode = args.only in (None, "decode")
+    run_gqe = args.only in (None, "gqe")
+
+    # ---- inputs, resident in HBM before any timing ----
+    if run_prefill:
+        pq, pk, pv = prefill_inputs(wp.B, wp.h, wp.g, wp.T, wp.d, "bf16", seed=wp.seed, device=dev)
+        pout = torch.empty_like(pq)
+        prefill_flops = 2.0 * wp.B * wp.h * wp.d * wp.T * (wp.T + 1)
+    if run_decode:
+        dq, dk, dv, dlens = decode_inputs(wd.B, wd.h, wd.g, wd.T, wd.d, wd.lens, seed=wd.seed,
+                                          device=dev)
+        dout = torch.empty_like(dq)
+        dws = torch.empty(max(gq.gqa_decode_workspace_bytes(wd.B, wd.h, wd.g, wd.T, wd.d), 1),
+                          dtype=torch.uint8, device=dev)
+        sum_lens = int(dlens.sum().item())
+        decode_bytes = (2 * wd.g * wd.d * 2) * sum_lens + 2 * dq.numel() * 2
+    if run_gqe:
+        gq_, gk, gv, glg = gqe_inputs(wg.B, wg.h, wg.g, wg.T, wg.d, "bf16", seed=wg.seed, device=dev)
+        gout = torch.empty_like(gq_)
+        dense_gqe_flops = 2.0 * wg.B * wg.h * wg.d * wg.T * (wg.T + 1)
+    torch.cuda.synchronize()
+
+    t_pre, t_dec = Timer(torch), Timer(torch)
+    t_gqe = {k: Timer(torch) for k in wg.top_k}
+    t_gqa_same = Timer(torch)  # dense GQA at the GQE shape, for the speedup ratio
+
+    def step(timed):
+        if run_prefill:
+            with (t_pre if timed else Timer(torch)):
+                gq.gqa_prefill(pq, pk, pv, causal=True, out=pout)
+        if run_decode:
+            flush.fill_(1)
+            with (t_dec if timed else Timer(torch)):
+                gq.gqa_decode(dq, dk, dv, dlens, out=dout, workspace=dws)
+        if run_gqe:
+            for kk in wg.top_k:
+                with (t_gqe[kk] if timed else Timer(torch)):
+                    gq.gqe_routed_prefill(gq_, gk, gv, glg, kk, causal=True, out=gout)
+            with (t_gqa_same if timed else Timer(torch)):
+                gq.gqa_prefill(gq_, gk, gv, causal=True, out=gout)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / max(args.steps, 1)
+
+    def stats(ms):
+        ms = sorted(ms)
+        return {"mean_ms": sum(ms) / len(ms), "median_ms": ms[len(ms) // 2], "min_ms": ms[0]}
+
+    res = {}
+    if run_prefill:
+        sp = stats(t_pre.ms())
+        tflops = prefill_flops / (sp["mean_ms"] * 1e-3) / 1e12
+        res["prefill"] = dict(sp, tflops=tflops, frac_peak=tflops / PEAK_BF16_TFLOPS,
+                              flops_per_launch=prefill_flops)
+        log(f"prefill: {sp['mean_ms']*1e3:.1f} us/launch, {tflops:.1f} TFLOP/s")
+    if run_decode:
+        sd = stats(t_dec.ms())
+        gbps = decode_bytes / (sd["mean_ms"] * 1e-3) / 1e9
+        res["decode"] = dict(sd, GBps=gbps, frac_peak=gbps / PEAK_HBM_GBPS,
+                             bytes_per_call=decode_bytes, sum_lens=sum_lens,
+                             kv_cache_bytes=gq.gqa_kv_cache_bytes(1, wd.g, sum_lens, wd.d))
+        log(f"decode: {sd['mean_ms']*1e3:.1f} us/call, {gbps:.0f} GB/s")
+    if run_gqe:
+        res["gqe"] = {}
+        dense_same = stats(t_gqa_same.ms())
+        for kk in wg.top_k:
+            sg = stats(t_gqe[kk].ms())
+            fl = dense_gqe_flops * kk / (wg.h // wg.g)
+            tf = fl / (sg["mean_ms"] * 1e-3) / 1e12
+            res["gqe"][f"top{kk}"] = dict(sg, tflops=tf, frac_peak=tf / PEAK_BF16_TFLOPS,
+                                          flops_per_call=fl,
+                                          speedup_vs_dense=dense_same["mean_ms"] / sg["mean_ms"])
+            log(f"gqe k={kk}: {sg['mean_ms']*1e3:.1f} us/call, {tf:.1f} TFLOP/s")
+
+    # ---- KV-group sweep (decode), outside the step ----
+    sweep = []
+    if run_decode and not args.no_sweep:
+        del dk, dv
+        ws = WORKLOADS["decode_sweep"]
+        for g in ws.g_sweep:
+            q, kc, vc, lens = decode_inputs(ws.B, ws.h, g, ws.T, ws.d, ws.lens, seed=ws.seed + g,
+                                            device=dev)
+            out = torch.empty_like(q)
+            wsb = torch.empty(max(gq.gqa_decode_workspace_bytes(ws.B, ws.h, g, ws.T, ws.d), 1),
+                              dtype=torch.uint8, device=dev)
+            tm = Timer(torch)
+            for it in range(3 + 10):
+                flush.fill_(1)
+                if it < 3:
+                    gq.gqa_decode(q, kc, vc, lens, out=out, workspace=wsb)
+                    continue
+                with tm:
+                    gq.gqa_decode(q, kc, vc, lens, out=out, workspace=wsb)
+            torch.cuda.synchronize()
+            st = stats(tm.ms())
+            kv = gq.gqa_kv_cache_bytes(ws.B, g, ws.T, ws.d)
+            nbytes = kv + 2 * q.numel() * 2
+            sweep.append(dict(g=g, heads_per_group=ws.h // g, kv_cache_bytes=kv,
+                              kv_bytes_over_2_nkv_d_T=kv / (2 * g * ws.d * ws.T),
+                              mean_ms=st["mean_ms"], GBps=nbytes / (st["mean_ms"] * 1e-3) / 1e9,
+                              frac_peak=nbytes / (st["mean_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS))
+            log(f"sweep g={g}: {st['mean_ms']*1e3:.1f} us, {sweep[-1]['GBps']:.0f} GB/s")
+            del q, kc, vc, out, wsb
+            torch.cuda.empty_cache()
+
+    # ---- CPU oracle baseline on a bounded sample of the prefill workload ----
+    cpu = None
+    if run_prefill and not args.no_cpu:
+        cpu = cpu_baseline(pq, pk, pv, wp)
+
+    line = {
+        "metric": METRIC,
+        "value": res["prefill"]["tflops"] if "prefill" in res else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "GQA causal prefill bf16/fp32-acc",
+            "B": wp.B, "h": wp.h, "g": wp.g, "T": wp.T, "d": wp.d, "causal": True,
+            "step": "prefill + decode(B=64,h=32,g=8,d=128,lens U[1024,8192]) + "
+                    "GQE(B=2,T=4096,h=32,g=8,d=128,k=1,2)",
+        },
+    }
+    if "prefill" in res:
+        p = res["prefill"]
+        line["roofline"] = {
+            "kernel": "attn_bf16_kernel<128,false>",
+            "bound": "mfma",
+            "achieved": p["tflops"],
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": p["tflops"] / PEAK_BF16_TFLOPS,
+            "traffic": traffic_for("prefill"),
+        }
+    if "decode" in res:
+        dd = res["decode"]
+        line["decode"] = {
+            "value": dd["GBps"], "unit": "GB/s", "frac": dd["frac_peak"],
+            "roofline": {"kernel": "decode_split_kernel<128,1> + decode_merge_kernel<128>",
+                         "bound": "hbm", "achieved": dd["GBps"], "peak": PEAK_HBM_GBPS,
+                         "unit": "GB/s", "frac": dd["frac_peak"],
+                         "traffic": traffic_for("decode")},
+            "mean_us": dd["mean_ms"] * 1e3, "bytes_per_call": dd["bytes_per_call"],
+        }
+    if "gqe" in res:
+        line["gqe"] = {k: {"tflops": v["tflops"], "frac": v["frac_peak"],
+                           "mean_us": v["mean_ms"] * 1e3,
+                           "speedup_vs_dense_gqa": v["speedup_vs_dense"]}
+                       for k, v in res["gqe"].items()}
+        line["gqe"]["dense_gqa_same_shape_us"] = dense_same["mean_ms"] * 1e3
+    if sweep:
+        line["decode_sweep"] = sweep
+    if cpu:
+        line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(pq, pk, pv, wp):
+    """Time the float64 oracle on the whole prefill workload (B=4, h=32, g=8,
+    T=2048, d=128, causal: 137.5 GFLOP of algorithmic work), on the same
+    inputs the GPU used."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    q, k, v = pq.cpu(), pk.cpu(), pv.cpu()
+    flops = 2.0 * wp.B * wp.h * wp.d * wp.T * (wp.T + 1)
+    log("cpu baseline: oracle on the whole prefill workload")
+    t0 = time.perf_counter()
+    out = oracle.gqa_ref(q, k, v, causal=True)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(out).all()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": dt,
+            "sample": "float64 oracle, whole prefill workload B=4 h=32 g=8 T=2048 d=128 causal "
+                      f"({flops/1e9:.2f} GFLOP algorithmic); host cpu_count={os.cpu_count()}"}
+
+
+if __name__ == "__main__":
+    main()
