@@ -37,6 +37,7 @@ constexpr int kBN = 64;                               // keys per KV tile
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerBlock = kWaves * 32;
+constexpr float kRescale = 8.0f;                      // lazy-rescale threshold, log2 units
 
 template <int D>
 struct Tile {
@@ -184,7 +185,12 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY;
+  // m_ref: the row's reference max (scaled, log2 units) that probabilities are
+  // taken against; identical in lanes l and l^32. It is raised only when a new
+  // score exceeds it by more than kRescale, so most tiles skip the rescale of
+  // the accumulators; probabilities stay below 2^kRescale and the final
+  // division by the row sum is exact whatever reference was used.
+  float m_ref = -INFINITY;
   float l_run = 0.0f;
 
   // Lane roles for the transposing V reads.
@@ -192,6 +198,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
   const int i16 = lane & 15;
   const int tr_row = 4 * hq + (i16 >> 2);
   const int tr_col = 16 * (grp & 1) + 4 * (i16 & 3);
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   load_tile(0);
   store_tile(0);
@@ -203,17 +210,30 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
     const int key0 = kt * kBN;
     const bool active = wave_has_rows && (!a.causal || key0 <= wt_hi);
     if (active) {
-      // S^T[key][row] for the 64 keys of this tile, two 32-key blocks.
+      // S^T[key][row] for the 64 keys of this tile, two 32-key blocks. The 8
+      // A-operand fragments of a block are read from LDS before its MFMAs.
       f32x16 s[2];
       const uint16_t* kl = Ks + buf * L::kElems;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
         const uint16_t* krow = kl + (kb * 32 + l32) * L::kPitch + hq * (D / 2);
+        bf16x8 kfr[D / 16];
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st)
-          s[kb] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(krow + 8 * st), qf[st], s[kb]);
+        for (int st = 0; st < D / 16; ++st) kfr[st] = *reinterpret_cast<const bf16x8*>(krow + 8 * st);
+        s[kb] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) s[kb] = mfma32x32x16(kfr[st], qf[st], s[kb]);
       }
+      // Keep several fragment reads in flight ahead of the MFMAs that use them
+      // (LDS latency is several MFMA issue slots).
+      constexpr int kAhead = 6, kFrags = 2 * (D / 16);
+      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+      for (int i = 0; i < kFrags - kAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
       // Mask keys past the row's limit: (kb, i) holds key key0 + 32kb + 8(i/4) + 4hq + i%4.
       const bool need_mask = (a.causal && key0 + kBN - 1 > wt_lo) || (key0 + kBN > a.T);
       if (need_mask) {
@@ -230,29 +250,30 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, s[kb][i]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run, mloc * a.c);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+        for (int i = 0; i < 16; i += 2) mloc = fmaxf(fmaxf(mloc, s[kb][i]), s[kb][i + 1]);
+      const float mloc_s = mloc * a.c;
+      if (__any(mloc_s > m_ref + kRescale)) {
+        const float m_new = fmaxf(m_ref, fmaxf(mloc_s, __shfl_xor(mloc_s, 32)));
+        const float alpha = fast_exp2(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+      }
 
       // P^T as bf16 B operands: step u covers keys 16u .. 16u+15 of the tile.
+      // The row sum adds the rounded bf16 values, the ones the MFMA uses.
       bf16x8 pf[4];
-      float psum = 0.0f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         float pv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pv[j] = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + j], a.c, -m_new));
-          psum += pv[j];
-        }
+        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + j], a.c, -m_ref));
         pf[u] = pack_bf16x8(pv);
+        const bf16x2* pp = reinterpret_cast<const bf16x2*>(&pf[u]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[j], ones, l_run, false);
       }
-      l_run += psum;
 
       // O^T += V^T P^T. Element j of step u is key 16u + 8(j/4) + 4hq + j%4,
       // which the two transposing reads fetch for d = 32db + l%32.
@@ -260,11 +281,12 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const uint16_t* p0 = vl + (16 * u + tr_row) * L::vPitch + tr_col;
+        bf16x8 vfr[D / 32];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 vf = lds_read_tr_pair(p0 + 32 * db, p0 + 8 * L::vPitch + 32 * db);
-          o[db] = mfma32x32x16(vf, pf[u], o[db]);
-        }
+        for (int db = 0; db < D / 32; ++db)
+          vfr[db] = lds_read_tr_pair(p0 + 32 * db, p0 + 8 * L::vPitch + 32 * db);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] = mfma32x32x16(vfr[db], pf[u], o[db]);
       }
     }
     if (kt + 1 < n_tiles) store_tile(buf ^ 1);
