@@ -72,7 +72,7 @@ struct DecodeLayout {
 
 DecodeLayout decode_layout(int B, int h, int g, int T_max, int d) {
   DecodeLayout L{};
-  L.chunk = gqa::decode_chunk(B, h, g, T_max);
+  L.chunk = gqa::decode_chunk(B, h, g, T_max, d);
   L.n_split = T_max > 0 ? (T_max + L.chunk - 1) / L.chunk : 1;
   if (L.n_split <= 1) return L;
   const size_t rows = (size_t)B * h * L.n_split;

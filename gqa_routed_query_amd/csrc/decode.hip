@@ -39,10 +39,13 @@ constexpr int kSub = 32;  // keys per wave sub-block
 
 template <int D>
 struct DTile {
+  static constexpr int kPitch = D + 8;   // 16-byte pad: A-operand reads of 16 rows hit distinct banks
   static constexpr int vPitch = D + 16;  // 32-byte pad: 8 rows of a transposing read hit distinct banks
+  static constexpr int kElems = kSub * kPitch;
   static constexpr int vElems = kSub * vPitch;
+  static constexpr int wElems = kElems + vElems;    // one wave's LDS staging area
   static constexpr int kCPR = D / 8;
-  static constexpr int kVLoads = kSub * kCPR / 64;  // 16-byte V loads per lane per sub-block
+  static constexpr int kLoads = kSub * kCPR / 64;   // 16-byte loads per lane per sub-block (K or V)
   static constexpr int kDS = D / 32;                // 32-wide reduction steps for S^T
 };
 
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(KArgs a) {
   using L = DTile<D>;
   constexpr int kComb = kWaves * 16 * (D + 2);  // floats per head block of the combine
   constexpr int kSmemBytes =
-      (kWaves * L::vElems * 2 > kComb * 4) ? kWaves * L::vElems * 2 : kComb * 4;
+      (kWaves * L::wElems * 2 > kComb * 4) ? kWaves * L::wElems * 2 : kComb * 4;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
 
   const int split = blockIdx.x % a.n_split;
@@ -95,7 +98,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(KArgs a) {
   const int lane = tid & 63;
   const int grp = lane >> 4;
   const int i16 = lane & 15;
-  uint16_t* Vw = reinterpret_cast<uint16_t*>(smem) + wave * L::vElems;
+  uint16_t* Kw = reinterpret_cast<uint16_t*>(smem) + wave * L::wElems;
+  uint16_t* Vw = Kw + L::kElems;
 
   // Q^T fragments: column = head hb*16 + l%16 of this group; lane group grp
   // holds d in [grp*D/4, grp*D/4 + D/4), 8 per reduction step.
@@ -128,36 +132,45 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(KArgs a) {
   const int tr_row = 4 * grp + (i16 >> 2);
   const int tr_col = 4 * (i16 & 3);
 
-  for (int sb0 = s0 + wave * kSub; sb0 < s1; sb0 += kWaves * kSub) {
-    // K rows in the A-operand layout, straight from HBM: lane holds key
-    // sb0 + 16kb + l%16 and d in [grp*D/4, grp*D/4 + D/4).
-    bf16x8 kf[2][L::kDS];
+  // Coalesced 16-byte loads of one 32-key sub-block of K and V into
+  // registers: chunk c = lane + 64i is row c / (D/8), column (c % (D/8)) * 8.
+  // Rows at or past s1 are not loaded (they may hold anything) and stage as 0.
+  uint4 kr[L::kLoads], vr[L::kLoads];
+  auto load_sub = [&](int sb0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = sb0 + 16 * kb + i16;
-      const uint16_t* krow = kbase + (size_t)key * D + grp * (D / 4);
-#pragma unroll
-      for (int ds = 0; ds < L::kDS; ++ds)
-        kf[kb][ds] = (key < s1) ? *reinterpret_cast<const bf16x8*>(krow + 8 * ds) : bf16x8{};
-    }
-    // V rows, coalesced, into the wave's LDS buffer (rows past s1 as zeros).
-    uint4 vr[L::kVLoads];
-#pragma unroll
-    for (int i = 0; i < L::kVLoads; ++i) {
+    for (int i = 0; i < L::kLoads; ++i) {
       const int cidx = lane + 64 * i;
       const int key = sb0 + cidx / L::kCPR;
-      const int col = (cidx % L::kCPR) * 8;
-      vr[i] = (key < s1) ? *reinterpret_cast<const uint4*>(vbase + (size_t)key * D + col)
-                         : make_uint4(0u, 0u, 0u, 0u);
+      const size_t off = (size_t)key * D + (cidx % L::kCPR) * 8;
+      const bool ok = key < s1;
+      kr[i] = ok ? *reinterpret_cast<const uint4*>(kbase + off) : make_uint4(0u, 0u, 0u, 0u);
+      vr[i] = ok ? *reinterpret_cast<const uint4*>(vbase + off) : make_uint4(0u, 0u, 0u, 0u);
     }
+  };
+  const int sb_first = s0 + wave * kSub;
+  if (sb_first < s1) load_sub(sb_first);
+  for (int sb0 = sb_first; sb0 < s1; sb0 += kWaves * kSub) {
+    // Stage this sub-block in the wave's LDS area, then start loading the
+    // next one so that its HBM reads overlap the math below.
 #pragma unroll
-    for (int i = 0; i < L::kVLoads; ++i) {
+    for (int i = 0; i < L::kLoads; ++i) {
       const int cidx = lane + 64 * i;
-      *reinterpret_cast<uint4*>(Vw + (cidx / L::kCPR) * L::vPitch + (cidx % L::kCPR) * 8) = vr[i];
+      const int row = cidx / L::kCPR, col = (cidx % L::kCPR) * 8;
+      *reinterpret_cast<uint4*>(Kw + row * L::kPitch + col) = kr[i];
+      *reinterpret_cast<uint4*>(Vw + row * L::vPitch + col) = vr[i];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (sb0 + kWaves * kSub < s1) load_sub(sb0 + kWaves * kSub);
+    // K in the A-operand layout: lane holds key sb0 + 16kb + l%16 and d in
+    // [grp*D/4, grp*D/4 + D/4), 8 per reduction step.
+    bf16x8 kf[2][L::kDS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ds = 0; ds < L::kDS; ++ds)
+        kf[kb][ds] = *reinterpret_cast<const bf16x8*>(Kw + (16 * kb + i16) * L::kPitch + grp * (D / 4) + 8 * ds);
 
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
@@ -327,25 +340,50 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D>
+const void* kernel_for_hb(int hb) {
+  if (hb == 1) return reinterpret_cast<const void*>(&decode_split_kernel<D, 1>);
+  if (hb == 2) return reinterpret_cast<const void*>(&decode_split_kernel<D, 2>);
+  if (hb <= 4) return reinterpret_cast<const void*>(&decode_split_kernel<D, 4>);
+  return nullptr;
+}
+
+const void* decode_kernel_for(int d, int hb) {
+  if (d == 64) return kernel_for_hb<64>(hb);
+  if (d == 128) return kernel_for_hb<128>(hb);
+  return nullptr;
+}
+
 }  // namespace
 
 bool decode_supports(int d) { return d == 64 || d == 128; }
 
-int decode_chunk(int B, int h, int g, int T_max) {
+int decode_chunk(int B, int h, int g, int T_max, int d) {
   if (const char* env = std::getenv("GQA_DECODE_CHUNK")) {
     const int c = std::atoi(env);
     if (c > 0) return div_up(c, 128) * 128;
   }
-  const int r = h / g;
-  // Enough blocks to fill the chip (about 4096), chunks long enough that the
-  // per-chunk partial (r heads x (d+2) floats) stays a few percent of the
-  // chunk's cache bytes.
-  const long long want = (long long)T_max * B * g / 4096;
-  int c = 128;
-  while (c < want && c < 4096) c *= 2;
-  const int floor_r = 32 * r;
-  while (c < floor_r && c < 4096) c *= 2;
-  return c;
+  // Few, long key streams: a block streams its chunk with one 32-key
+  // sub-block per wave in flight, and per-chunk costs (first-load latency,
+  // the block combine, the partial write and the merge) favour long chunks.
+  // Split only as far as needed to give every block slot of the chip work.
+  int n_cu = 256, per_cu = 2;
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) n_cu = v;
+    const void* fn = decode_kernel_for(d, div_up(h / g, 16));
+    int blocks = 0;
+    if (fn && hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kThreads, 0) == hipSuccess &&
+        blocks > 0)
+      per_cu = blocks;
+  }
+  (void)hipGetLastError();
+  const long long streams = (long long)B * g;
+  const long long want = (long long)per_cu * n_cu;
+  const int n_split = streams >= want ? 1 : (int)((want + streams - 1) / streams);
+  const int c = div_up(div_up(T_max, n_split), 128) * 128;
+  return c > 0 ? c : 128;
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {

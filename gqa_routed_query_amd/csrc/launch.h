@@ -62,6 +62,6 @@ bool attn_f32_supports(int d);
 bool decode_supports(int d);
 
 // Decode split size in keys for a problem shape (honours GQA_DECODE_CHUNK).
-int decode_chunk(int B, int h, int g, int T_max);
+int decode_chunk(int B, int h, int g, int T_max, int d);
 
 }  // namespace gqa
