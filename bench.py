@@ -144,8 +144,8 @@ def main():
         dq, dk, dv, dlens = decode_inputs(wd.B, wd.h, wd.g, wd.T, wd.d, wd.lens, seed=wd.seed,
                                           device=dev)
         dout = torch.empty_like(dq)
-        dws = torch.empty(max(gq.gqa_decode_workspace_bytes(wd.B, wd.h, wd.g, wd.T, wd.d), 1),
-                          dtype=torch.uint8, device=dev)
+        dws_bytes = gq.gqa_decode_workspace_bytes(wd.B, wd.h, wd.g, wd.T, wd.d)
+        dws = torch.empty(max(dws_bytes, 1), dtype=torch.uint8, device=dev)
         sum_lens = int(dlens.sum().item())
         decode_bytes = (2 * wd.g * wd.d * 2) * sum_lens + 2 * dq.numel() * 2
     if run_gqe:
@@ -286,7 +286,7 @@ def main():
         dd = res["decode"]
         line["decode"] = {
             "value": dd["GBps"], "unit": "GB/s", "frac": dd["frac_peak"],
-            "roofline": {"kernel": "decode_split_kernel<128,1> + decode_merge_kernel<128>",
+            "roofline": {"kernel": "decode_split_kernel<128,1>" + (" + decode_merge_kernel<128>" if dws_bytes else ""),
                          "bound": "hbm", "achieved": dd["GBps"], "peak": PEAK_HBM_GBPS,
                          "unit": "GB/s", "frac": dd["frac_peak"],
                          "traffic": traffic_for("decode")},
