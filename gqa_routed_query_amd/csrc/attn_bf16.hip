@@ -11,11 +11,17 @@
 // multiplies each row by its gate.
 //
 // Design for CDNA4:
-//  * A workgroup owns 256 attention rows of one (batch, KV group): rows are
+//  * A workgroup owns 192 attention rows of one (batch, KV group): rows are
 //    (token, slot) pairs in token-major order, so one K/V tile staged in LDS is
 //    shared by every query head of the group (the GQA reuse), and a routed
 //    problem is just a shorter row list with a head lookup per row.
-//  * 8 waves x 32 rows. Scores are computed transposed, S^T = K Q^T, with
+//  * 6 waves x 32 rows per workgroup, two workgroups per CU, three waves per
+//    SIMD: the kernel is latency-bound (LDS fragment reads, MFMA -> softmax
+//    -> MFMA dependencies, barriers), so 32-key tiles keep the register budget
+//    at three waves per SIMD, which hides more of those latencies than larger
+//    tiles at two waves per SIMD, and small workgroups keep short routed
+//    problems spread over every CU.
+//    Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16 so that each lane ends up owning one query row
 //    (column l%32); the probabilities are then already in the B-operand layout
 //    of O^T += V^T P^T, and the online-softmax statistics of a row live in two
@@ -33,21 +39,24 @@
 namespace gqa {
 namespace {
 
-constexpr int kBN = 64;                               // keys per KV tile
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerBlock = kWaves * 32;
+// Two configurations: 12 waves with 32-key tiles (three waves per SIMD) for
+// large grids, and 8 waves with 64-key tiles (two waves per SIMD, half the
+// per-tile overhead) when a 12-wave grid would leave compute units without
+// two workgroups' worth of work (short routed problems).
+constexpr int kWavesLarge = 12, kBNLarge = 32;
+constexpr int kWavesSmall = 8, kBNSmall = 64;
 constexpr float kRescale = 8.0f;                      // lazy-rescale threshold, log2 units
 
-template <int D>
+template <int D, int W, int kBN>
 struct Tile {
+  static constexpr int kThreads = W * 64;
   static constexpr int kPitch = D + 8;    // 16-byte pad: A-operand reads of 16 rows hit distinct banks
   static constexpr int vPitch = D + 32;   // 64-byte pad: transposing reads of 4 rows hit distinct banks
   static constexpr int kElems = kBN * kPitch;
   static constexpr int vElems = kBN * vPitch;
   static constexpr int kCPR = D / 8;      // 16-byte chunks per row
-  static constexpr int kLoads = kBN * kCPR / kThreads;
-  static_assert(kBN * kCPR % kThreads == 0, "tile must split evenly over the block");
+  static constexpr int kChunks = kBN * kCPR;
+  static constexpr int kLoads = (kChunks + kThreads - 1) / kThreads;
 };
 
 struct KArgs {
@@ -66,8 +75,9 @@ struct KArgs {
 
 // Zero the output rows of heads the router did not keep, for the tokens whose
 // first row lies in this block's row range.
-template <int D>
+template <int D, int W>
 __device__ void zero_unselected_rows(const KArgs& a, int b, int gam, int row0, int n_rows) {
+  constexpr int kThreads = W * 64, kRowsPerBlock = W * 32;
   const int R = a.R, r = a.r;
   const int t_lo = div_up(row0, R);
   const int t_hi = (min(row0 + kRowsPerBlock, n_rows) - 1) / R;
@@ -97,9 +107,10 @@ __device__ void zero_unselected_rows(const KArgs& a, int b, int gam, int row0, i
   }
 }
 
-template <int D, bool ROUTED>
-__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
-  using L = Tile<D>;
+template <int D, int W, int kBN, bool ROUTED>
+__global__ __launch_bounds__(W * 64) void attn_bf16_kernel(KArgs a) {
+  using L = Tile<D, W, kBN>;
+  constexpr int kThreads = W * 64, kRowsPerBlock = W * 32;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (L::kElems + L::vElems)];
   uint16_t* Ks = smem;
   uint16_t* Vs = smem + 2 * L::kElems;
@@ -117,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
   const int n_rows = a.T * a.R;
   const int row0 = tile * kRowsPerBlock;
 
-  if (ROUTED && a.zero_unselected) zero_unselected_rows<D>(a, b, gam, row0, n_rows);
+  if (ROUTED && a.zero_unselected) zero_unselected_rows<D, W>(a, b, gam, row0, n_rows);
 
   // This lane's attention row.
   const int rho = row0 + wave * 32 + l32;
@@ -162,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
       const int c = tid + i * kThreads;
       const int key = kt * kBN + c / L::kCPR;
       const int col = (c % L::kCPR) * 8;
-      if (key < a.T) {
+      if (c < L::kChunks && key < a.T) {
         rk[i] = *reinterpret_cast<const uint4*>(kbase + (size_t)key * D + col);
         rv[i] = *reinterpret_cast<const uint4*>(vbase + (size_t)key * D + col);
       } else {
@@ -175,6 +186,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
 #pragma unroll
     for (int i = 0; i < L::kLoads; ++i) {
       const int c = tid + i * kThreads;
+      if (c >= L::kChunks) continue;
       const int row = c / L::kCPR;
       const int col = (c % L::kCPR) * 8;
       *reinterpret_cast<uint4*>(Ks + buf * L::kElems + row * L::kPitch + col) = rk[i];
@@ -212,10 +224,10 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
     if (active) {
       // S^T[key][row] for the 64 keys of this tile, two 32-key blocks. The 8
       // A-operand fragments of a block are read from LDS before its MFMAs.
-      f32x16 s[2];
+      f32x16 s[kBN / 32];
       const uint16_t* kl = Ks + buf * L::kElems;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kBN / 32; ++kb) {
         const uint16_t* krow = kl + (kb * 32 + l32) * L::kPitch + hq * (D / 2);
         bf16x8 kfr[D / 16];
 #pragma unroll
@@ -226,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
       }
       // Keep several fragment reads in flight ahead of the MFMAs that use them
       // (LDS latency is several MFMA issue slots).
-      constexpr int kAhead = 6, kFrags = 2 * (D / 16);
+      constexpr int kAhead = 6, kFrags = (kBN / 32) * (D / 16);
       __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
       for (int i = 0; i < kFrags - kAhead; ++i) {
@@ -239,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
       if (need_mask) {
         const int lim = a.causal ? t_row : a.T - 1;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * hq + (i & 3);
@@ -248,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
       }
       float mloc = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) mloc = fmaxf(fmaxf(mloc, s[kb][i]), s[kb][i + 1]);
       const float mloc_s = mloc * a.c;
@@ -263,9 +275,9 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
 
       // P^T as bf16 B operands: step u covers keys 16u .. 16u+15 of the tile.
       // The row sum adds the rounded bf16 values, the ones the MFMA uses.
-      bf16x8 pf[4];
+      bf16x8 pf[kBN / 16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kBN / 16; ++u) {
         float pv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + j], a.c, -m_ref));
@@ -279,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
       // which the two transposing reads fetch for d = 32db + l%32.
       const uint16_t* vl = Vs + buf * L::vElems;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kBN / 16; ++u) {
         const uint16_t* p0 = vl + (16 * u + tr_row) * L::vPitch + tr_col;
         bf16x8 vfr[D / 32];
 #pragma unroll
@@ -314,6 +326,17 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(KArgs a) {
   }
 }
 
+template <int D, int W, int BN>
+hipError_t launch_dw(KArgs a, const AttnParams& p, hipStream_t stream) {
+  a.n_row_tiles = div_up(p.T * p.R, W * 32);
+  const dim3 grid(a.n_row_tiles * a.BG), block(W * 64);
+  if (p.idx)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, W, BN, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, W, BN, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
   KArgs a;
@@ -328,18 +351,18 @@ hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
   a.T = p.T;
   a.R = p.R;
   a.r = p.h / p.g;
-  a.n_row_tiles = div_up(p.T * p.R, kRowsPerBlock);
   a.BG = p.B * p.g;
   a.c = p.scale * kLog2e;
   a.causal = p.causal;
   a.out_bf16 = p.out_bf16;
   a.zero_unselected = p.zero_unselected;
-  const dim3 grid(a.n_row_tiles * a.BG), block(kThreads);
-  if (p.idx)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, true>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, false>), grid, block, 0, stream, a);
-  return hipGetLastError();
+  int n_cu = 256, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n_cu = 256;
+  const long long large_grid = (long long)a.BG * div_up(p.T * p.R, kWavesLarge * 32);
+  if (large_grid >= 2ll * n_cu) return launch_dw<D, kWavesLarge, kBNLarge>(a, p, stream);
+  return launch_dw<D, kWavesSmall, kBNSmall>(a, p, stream);
 }
 
 }  // namespace
