@@ -274,7 +274,7 @@ def main():
     if "prefill" in res:
         p = res["prefill"]
         line["roofline"] = {
-            "kernel": "attn_bf16_kernel<128,false>",
+            "kernel": "attn_bf16_kernel<128,12,32,false>",
             "bound": "mfma",
             "achieved": p["tflops"],
             "peak": PEAK_BF16_TFLOPS,
@@ -286,7 +286,7 @@ def main():
         dd = res["decode"]
         line["decode"] = {
             "value": dd["GBps"], "unit": "GB/s", "frac": dd["frac_peak"],
-            "roofline": {"kernel": "decode_split_kernel<128,1>" + (" + decode_merge_kernel<128>" if dws_bytes else ""),
+            "roofline": {"kernel": "decode_kernel<128,1> + decode_merge_kernel<128>",
                          "bound": "hbm", "achieved": dd["GBps"], "peak": PEAK_HBM_GBPS,
                          "unit": "GB/s", "frac": dd["frac_peak"],
                          "traffic": traffic_for("decode")},

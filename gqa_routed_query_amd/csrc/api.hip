@@ -66,16 +66,15 @@ gqa_status hip_status(hipError_t e, const char* what) {
 }
 
 struct DecodeLayout {
-  int chunk, n_split;
+  int n_units;
   size_t acc_bytes, ml_bytes, total;
 };
 
-DecodeLayout decode_layout(int B, int h, int g, int T_max, int d) {
+// Two partials (r heads each) per wave of the decode grid.
+DecodeLayout decode_layout(int h, int g, int d) {
   DecodeLayout L{};
-  L.chunk = gqa::decode_chunk(B, h, g, T_max, d);
-  L.n_split = T_max > 0 ? (T_max + L.chunk - 1) / L.chunk : 1;
-  if (L.n_split <= 1) return L;
-  const size_t rows = (size_t)B * h * L.n_split;
+  L.n_units = gqa::decode_units(h, g, d);
+  const size_t rows = (size_t)L.n_units * 2 * (h / g);
   L.acc_bytes = (rows * d * sizeof(float) + 255) & ~(size_t)255;
   L.ml_bytes = rows * 2 * sizeof(float);
   L.total = L.acc_bytes + L.ml_bytes;
@@ -129,7 +128,7 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, void* out, i
 
 size_t gqa_decode_workspace_bytes(int B, int h, int g, int T_max, int d) {
   if (B <= 0 || h < 1 || g < 1 || h % g || T_max <= 0 || d <= 0) return 0;
-  return decode_layout(B, h, g, T_max, d).total;
+  return decode_layout(h, g, d).total;
 }
 
 gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* lens,
@@ -155,7 +154,7 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache, c
   if (in_dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "decode supports bf16 caches only");
   if (!gqa::decode_supports(d)) return fail(GQA_ERR_UNSUPPORTED, "decode supports d in {64, 128}, got %d", d);
   if (h / g > 64) return fail(GQA_ERR_UNSUPPORTED, "decode supports h/g <= 64, got %d", h / g);
-  const DecodeLayout L = decode_layout(B, h, g, T_max > 0 ? T_max : 1, d);
+  const DecodeLayout L = decode_layout(h, g, d);
   if (workspace_bytes < L.total)
     return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, L.total);
   if (L.total && (!workspace || !aligned16(workspace)))
@@ -165,10 +164,9 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache, c
   gqa::DecodeParams p{};
   p.q = q; p.k_cache = k_cache; p.v_cache = v_cache; p.lens = lens; p.out = out;
   p.B = B; p.h = h; p.g = g; p.T_max = T_max; p.d = d;
-  p.chunk = L.chunk;
-  p.n_split = L.n_split;
-  p.part_acc = L.total ? static_cast<float*>(workspace) : nullptr;
-  p.part_ml = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.acc_bytes) : nullptr;
+  p.n_units = L.n_units;
+  p.part_acc = static_cast<float*>(workspace);
+  p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.acc_bytes);
   p.scale = scale;
   p.out_bf16 = out_dtype == GQA_BF16;
   return hip_status(gqa::launch_decode(p, static_cast<hipStream_t>(stream)), "gqa_decode launch");

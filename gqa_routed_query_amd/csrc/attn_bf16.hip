@@ -11,16 +11,17 @@
 // multiplies each row by its gate.
 //
 // Design for CDNA4:
-//  * A workgroup owns 192 attention rows of one (batch, KV group): rows are
+//  * A workgroup owns W*32 attention rows of one (batch, KV group): rows are
 //    (token, slot) pairs in token-major order, so one K/V tile staged in LDS is
 //    shared by every query head of the group (the GQA reuse), and a routed
 //    problem is just a shorter row list with a head lookup per row.
-//  * 6 waves x 32 rows per workgroup, two workgroups per CU, three waves per
-//    SIMD: the kernel is latency-bound (LDS fragment reads, MFMA -> softmax
-//    -> MFMA dependencies, barriers), so 32-key tiles keep the register budget
-//    at three waves per SIMD, which hides more of those latencies than larger
-//    tiles at two waves per SIMD, and small workgroups keep short routed
-//    problems spread over every CU.
+//  * Each wave owns 32 rows. Large grids use 12 waves with 32-key tiles: the
+//    kernel is latency-bound (LDS fragment reads, MFMA -> softmax -> MFMA
+//    dependencies, barriers), and the small tile keeps registers within three
+//    waves per SIMD, which hides more of those latencies than larger tiles at
+//    two waves per SIMD. Grids too small to give every CU two such workgroups
+//    (short routed problems) use 8 waves with 64-key tiles instead, halving the
+//    per-tile overhead and spreading the rows over more workgroups.
 //    Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16 so that each lane ends up owning one query row
 //    (column l%32); the probabilities are then already in the B-operand layout

@@ -10,21 +10,34 @@
 // GQA shrinks it by h/g.
 //
 // Design for CDNA4 (HBM-bound):
-//  * A workgroup of 4 waves owns one (batch, KV group, key chunk). Every cached
-//    K/V row of the chunk is read once, with coalesced 16-byte loads, and
-//    serves all h/g query heads of the group from registers.
-//  * Per 32-key sub-block a wave computes S^T = K Q^T with
-//    v_mfma_f32_16x16x32_bf16 (heads are the 16-wide B columns; groups with
-//    fewer than 16 heads leave columns idle -- the matrix cores have far more
-//    headroom than HBM), runs the online softmax on its lanes, and accumulates
-//    O^T += V^T P^T with V transposed by ds_read_b64_tr_b16 from a wave-private
-//    LDS buffer.
-//  * The 4 waves combine their (max, sum, accumulator) in LDS and the block
-//    writes one partial per (head, chunk); a second kernel merges the chunks
-//    by log-sum-exp. A problem with a single chunk skips the merge and writes
-//    the normalised output directly.
-//  * Cache rows at or beyond lens[b] are never loaded: padding may hold
-//    anything, NaN included.
+//  * Work is balanced over the keys, not over sequences. The cached keys of
+//    all (batch, KV group) streams, laid end to end, form one key range; every
+//    workgroup of the grid takes an equal contiguous share of it (computed on
+//    the device from lens), so sequences of very different lengths still keep
+//    every CU streaming until the end. One grid holds exactly the workgroups
+//    the chip keeps resident.
+//  * A share crosses stream boundaries. A stream that lies wholly in one
+//    share is finished by that workgroup, which writes the output rows; a
+//    stream cut by share boundaries leaves one partial (max, sum, accumulator
+//    per head) per piece, and a second kernel merges the pieces by
+//    log-sum-exp. A workgroup writes at most two partials: for its first and
+//    its last stream.
+//  * Inside a piece the 4 waves take interleaved 32-key sub-blocks, so the
+//    workgroup reads 128 consecutive cache rows (32 KiB of K, 32 KiB of V) per
+//    step. Every cached K/V row is read once, with coalesced 16-byte loads
+//    into registers, staged through a wave-private padded LDS buffer, and
+//    serves all h/g query heads of its group. A wave's next sub-block (also in
+//    a later piece) is loading while the current one is multiplied; at the end
+//    of a piece the waves combine their (max, sum, accumulator) through LDS.
+//  * Per 32-key sub-block: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (heads are
+//    the 16-wide B columns; groups with fewer than 16 heads leave columns
+//    idle -- the matrix cores have far more headroom than HBM), the online
+//    softmax with a lazily raised reference max, and O^T += V^T P^T with V
+//    transposed by ds_read_b64_tr_b16.
+//  * Cache rows at or beyond lens[b] are never loaded: a sub-block's rows past
+//    the end of its piece re-read the piece's last row (always a valid row)
+//    and are masked out of the softmax. Padding may hold anything, NaN
+//    included.
 #include <cstdlib>
 
 #include "common.h"
@@ -33,9 +46,11 @@
 namespace gqa {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;            // waves per workgroup; they share one key share
 constexpr int kThreads = kWaves * 64;
-constexpr int kSub = 32;  // keys per wave sub-block
+constexpr int kSub = 32;             // keys per sub-block
+constexpr int kMinShare = 256;       // smallest key share per workgroup
+constexpr float kRescale = 8.0f;     // lazy-rescale threshold, log2 units
 
 template <int D>
 struct DTile {
@@ -55,255 +70,458 @@ struct KArgs {
   const uint16_t* vc;
   const int32_t* lens;
   void* out;
-  float* part_acc;
-  float* part_ml;
-  int h, g, r, T_max;
-  int chunk, n_split;
-  float c;
+  float* part_acc;  // [n_units, 2, r, D]
+  float* part_ml;   // [n_units, 2, r, 2]: reference max (log2 units), sum
+  int B, h, g, r, T_max;
+  int n_units;      // workgroups sharing the key range
+  float c;          // scale * log2(e)
   int out_bf16;
 };
 
-template <int D, int HB>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(KArgs a) {
-  using L = DTile<D>;
-  constexpr int kComb = kWaves * 16 * (D + 2);  // floats per head block of the combine
-  constexpr int kSmemBytes =
-      (kWaves * L::wElems * 2 > kComb * 4) ? kWaves * L::wElems * 2 : kComb * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
+__device__ __forceinline__ int seq_len(const KArgs& a, int b) {
+  return min(max(a.lens[b], 0), a.T_max);
+}
 
-  const int split = blockIdx.x % a.n_split;
-  const int bg = blockIdx.x / a.n_split;
-  const int b = bg / a.g;
-  const int gam = bg - b * a.g;
-  const int len = min(max(a.lens[b], 0), a.T_max);
-  const int s0 = split * a.chunk;
-  const int tid = threadIdx.x;
-  if (s0 >= len) {
-    // The merge never reads chunks past lens[b]; with a single chunk there is
-    // no merge, so an empty sequence writes its zero rows here.
-    if (a.n_split == 1) {
-      for (int x = tid; x < a.r * D; x += kThreads) {
-        const size_t off = ((size_t)b * a.h + gam * a.r) * D + x;
-        if (a.out_bf16)
-          static_cast<uint16_t*>(a.out)[off] = 0;
-        else
-          static_cast<float*>(a.out)[off] = 0.0f;
-      }
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Keys of all streams: g * sum_b lens[b]. Every lane returns the total.
+__device__ __forceinline__ long long total_keys(const KArgs& a, int lane) {
+  long long t = 0;
+  for (int b = lane; b < a.B; b += 64) t += seq_len(a, b);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+  return t * a.g;
+}
+
+// The equal share of the key range each wave takes.
+__device__ __forceinline__ long long share_of(long long total, int n_units) {
+  const long long p = (total + n_units - 1) / n_units;
+  return p > kMinShare ? p : (long long)kMinShare;
+}
+
+// A piece of one stream: keys [k0, k1) of stream (b, gam), which has len keys.
+struct Piece {
+  int b, gam, k0, k1, len;
+};
+
+// The stream holding global key position pos (< total), as a piece starting
+// there and ending at min(stream end, pos + avail).
+__device__ __forceinline__ Piece locate(const KArgs& a, long long pos, long long avail, int lane) {
+  long long base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int b = b0 + lane;
+    const int len = b < a.B ? seq_len(a, b) : 0;
+    const long long n = (long long)a.g * len;
+    long long incl = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
     }
-    return;
+    const long long lo = base + incl - n;
+    const unsigned long long hit = __ballot(lo <= pos && pos < base + incl);
+    if (hit) {
+      const int src = __ffsll(hit) - 1;
+      const int sl = uniform(__shfl(len, src));
+      const long long off = pos - __shfl(lo, src);
+      Piece p;
+      p.b = uniform(b0 + src);
+      p.len = sl;
+      p.gam = uniform((int)(off / sl));
+      p.k0 = uniform((int)(off - (long long)p.gam * sl));
+      p.k1 = (int)min((long long)sl, p.k0 + avail);
+      p.k1 = uniform(p.k1);
+      return p;
+    }
+    base += __shfl(incl, 63);
   }
-  const int s1 = min(s0 + a.chunk, len);
+  return Piece{a.B, 0, 0, 0, 0};  // not reached for pos < total
+}
 
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int grp = lane >> 4;
-  const int i16 = lane & 15;
-  uint16_t* Kw = reinterpret_cast<uint16_t*>(smem) + wave * L::wElems;
-  uint16_t* Vw = Kw + L::kElems;
+// The piece after p, if this wave's share [.., end) goes on past it; pos is
+// the global position of p.k0 and is advanced to the next piece's start.
+__device__ __forceinline__ bool next_piece(const KArgs& a, const Piece& p, long long& pos, long long end, Piece& n) {
+  pos += p.k1 - p.k0;
+  if (pos >= end) return false;
+  n = p;
+  n.k0 = 0;
+  if (p.gam + 1 < a.g) {
+    n.gam = p.gam + 1;
+  } else {
+    n.gam = 0;
+    int b = p.b + 1;
+    while (seq_len(a, b) == 0) ++b;  // pos < total: a non-empty stream follows
+    n.b = uniform(b);
+    n.len = uniform(seq_len(a, b));
+  }
+  n.k1 = uniform((int)min((long long)n.len, end - pos));
+  return true;
+}
 
-  // Q^T fragments: column = head hb*16 + l%16 of this group; lane group grp
-  // holds d in [grp*D/4, grp*D/4 + D/4), 8 per reduction step.
-  bf16x8 qf[HB][L::kDS];
+template <int D, int HB>
+__device__ __forceinline__ void load_q(const KArgs& a, const Piece& p, int grp, int i16,
+                                       bf16x8 (&qf)[HB][DTile<D>::kDS]) {
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int e = hb * 16 + i16;
-    const uint16_t* qrow = a.q + ((size_t)b * a.h + gam * a.r + min(e, a.r - 1)) * D + grp * (D / 4);
+    const uint16_t* qrow =
+        a.q + ((size_t)p.b * a.h + p.gam * a.r + min(e, a.r - 1)) * D + grp * (D / 4);
 #pragma unroll
-    for (int ds = 0; ds < L::kDS; ++ds) {
+    for (int ds = 0; ds < DTile<D>::kDS; ++ds) {
       bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 8 * ds);
       if (e >= a.r) x = bf16x8{};
       qf[hb][ds] = x;
     }
   }
+}
 
-  f32x4 o[HB][D / 16];
-  float m_run[HB], l_run[HB];
+// Coalesced 16-byte loads of one 32-key sub-block of K and V into registers:
+// chunk c = lane + 64i is row c / (D/8), column (c % (D/8)) * 8. Rows at or
+// past the piece end k1 re-read row k1-1 (masked out of the softmax later).
+template <int D>
+__device__ __forceinline__ void load_sub(const KArgs& a, const Piece& p, int sb0, int lane,
+                                         u32x4 (&kr)[DTile<D>::kLoads], u32x4 (&vr)[DTile<D>::kLoads]) {
+  using L = DTile<D>;
+  const size_t base = ((size_t)p.b * a.g + p.gam) * a.T_max * D;
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    m_run[hb] = -INFINITY;
-    l_run[hb] = 0.0f;
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) o[hb][db] = f32x4{};
+  for (int i = 0; i < L::kLoads; ++i) {
+    const int cidx = lane + 64 * i;
+    const int key = min(sb0 + cidx / L::kCPR, p.k1 - 1);
+    const size_t off = base + (size_t)key * D + (cidx % L::kCPR) * 8;
+    kr[i] = *reinterpret_cast<const u32x4*>(a.kc + off);
+    vr[i] = *reinterpret_cast<const u32x4*>(a.vc + off);
   }
+}
 
-  const size_t cache_base = (size_t)bg * a.T_max * D;
-  const uint16_t* kbase = a.kc + cache_base;
-  const uint16_t* vbase = a.vc + cache_base;
-  const int tr_row = 4 * grp + (i16 >> 2);
-  const int tr_col = 4 * (i16 & 3);
-
-  // Coalesced 16-byte loads of one 32-key sub-block of K and V into
-  // registers: chunk c = lane + 64i is row c / (D/8), column (c % (D/8)) * 8.
-  // Rows at or past s1 are not loaded (they may hold anything) and stage as 0.
-  uint4 kr[L::kLoads], vr[L::kLoads];
-  auto load_sub = [&](int sb0) {
-#pragma unroll
-    for (int i = 0; i < L::kLoads; ++i) {
-      const int cidx = lane + 64 * i;
-      const int key = sb0 + cidx / L::kCPR;
-      const size_t off = (size_t)key * D + (cidx % L::kCPR) * 8;
-      const bool ok = key < s1;
-      kr[i] = ok ? *reinterpret_cast<const uint4*>(kbase + off) : make_uint4(0u, 0u, 0u, 0u);
-      vr[i] = ok ? *reinterpret_cast<const uint4*>(vbase + off) : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  const int sb_first = s0 + wave * kSub;
-  if (sb_first < s1) load_sub(sb_first);
-  for (int sb0 = sb_first; sb0 < s1; sb0 += kWaves * kSub) {
-    // Stage this sub-block in the wave's LDS area, then start loading the
-    // next one so that its HBM reads overlap the math below.
-#pragma unroll
-    for (int i = 0; i < L::kLoads; ++i) {
-      const int cidx = lane + 64 * i;
-      const int row = cidx / L::kCPR, col = (cidx % L::kCPR) * 8;
-      *reinterpret_cast<uint4*>(Kw + row * L::kPitch + col) = kr[i];
-      *reinterpret_cast<uint4*>(Vw + row * L::vPitch + col) = vr[i];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (sb0 + kWaves * kSub < s1) load_sub(sb0 + kWaves * kSub);
-    // K in the A-operand layout: lane holds key sb0 + 16kb + l%16 and d in
-    // [grp*D/4, grp*D/4 + D/4), 8 per reduction step.
-    bf16x8 kf[2][L::kDS];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ds = 0; ds < L::kDS; ++ds)
-        kf[kb][ds] = *reinterpret_cast<const bf16x8*>(Kw + (16 * kb + i16) * L::kPitch + grp * (D / 4) + 8 * ds);
-
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      // S^T[key][head]: lane holds keys sb0 + 16kb + 4grp + i for its head column.
-      f32x4 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x4{};
-#pragma unroll
-        for (int ds = 0; ds < L::kDS; ++ds) s[kb] = mfma16x16x32(kf[kb][ds], qf[hb][ds], s[kb]);
-      }
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (sb0 + 16 * kb + 4 * grp + i >= s1) s[kb][i] = -INFINITY;
-          mloc = fmaxf(mloc, s[kb][i]);
-        }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run[hb], mloc * a.c);
-      const float alpha = fast_exp2(m_run[hb] - m_new);
-      m_run[hb] = m_new;
-      float pv[8];
-      float psum = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pv[j] = fast_exp2(fmaf(s[j >> 2][j & 3], a.c, -m_new));
-        psum += pv[j];
-      }
-      l_run[hb] = l_run[hb] * alpha + psum;
-      const bf16x8 pf = pack_bf16x8(pv);
-      // O^T += V^T P^T: element j is key 4grp + j (j < 4) or 16 + 4grp + j-4.
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const uint16_t* p0 = Vw + tr_row * L::vPitch + 16 * db + tr_col;
-        const bf16x8 vf = lds_read_tr_pair(p0, p0 + 16 * L::vPitch);
-        o[hb][db] = mfma16x16x32(vf, pf, o[hb][db] * alpha);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
+// The sub-block of this wave that follows (p, sb) in the block's piece
+// sequence: the next one of the piece, else the wave's first one in a later
+// piece (pieces shorter than 32 * wave keys have none for this wave). pos is
+// the global position of p.k0 and moves along with p. False when the share
+// has no further sub-block for this wave.
+__device__ __forceinline__ bool next_sub(const KArgs& a, Piece& p, long long& pos, long long end,
+                                         int& sb, int& pi, int wave) {
+  if (sb + kWaves * kSub < p.k1) {
+    sb += kWaves * kSub;
+    return true;
   }
-
-  // Combine the 4 waves, one head block at a time, through LDS.
-  float* comb = reinterpret_cast<float*>(smem);
-  const bool single = (a.n_split == 1);
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    float lsum = l_run[hb];
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    __syncthreads();  // LDS is free (V buffers or the previous head block)
-    float* w = comb + (wave * 16 + i16) * (D + 2);
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[16 * db + 4 * grp + i] = o[hb][db][i];
-    if (grp == 0) {
-      w[D] = m_run[hb];
-      w[D + 1] = lsum;
-    }
-    __syncthreads();
-    // 16 heads x D values over 256 threads.
-    for (int x = tid; x < 16 * D; x += kThreads) {
-      const int hh = x / D;
-      const int d = x - hh * D;
-      const int e = hb * 16 + hh;
-      float M = -INFINITY;
-#pragma unroll
-      for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, comb[(wv * 16 + hh) * (D + 2) + D]);
-      float acc = 0.0f, den = 0.0f;
-#pragma unroll
-      for (int wv = 0; wv < kWaves; ++wv) {
-        const float* src = comb + (wv * 16 + hh) * (D + 2);
-        const float mw = src[D];
-        const float sc = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
-        acc += sc * src[d];
-        den += sc * src[D + 1];
-      }
-      if (e < a.r) {
-        const size_t row = (size_t)b * a.h + gam * a.r + e;
-        if (single) {
-          const float y = acc / den;
-          if (a.out_bf16)
-            static_cast<uint16_t*>(a.out)[row * D + d] = static_cast<uint16_t>(pack_bf16x2(y, 0.0f) & 0xffffu);
-          else
-            static_cast<float*>(a.out)[row * D + d] = y;
-        } else {
-          const size_t pidx = row * a.n_split + split;
-          a.part_acc[pidx * D + d] = acc;
-          if (d == 0) {
-            a.part_ml[pidx * 2 + 0] = M;
-            a.part_ml[pidx * 2 + 1] = den;
-          }
-        }
-      }
+  while (true) {
+    Piece n;
+    if (!next_piece(a, p, pos, end, n)) return false;
+    p = n;
+    ++pi;
+    if (wave * kSub < p.k1) {
+      sb = wave * kSub;
+      return true;
     }
   }
 }
 
-// One wave per (batch, head): merge the chunk partials by log-sum-exp.
+template <int D, int HB>
+__global__ __launch_bounds__(kThreads) void decode_kernel(KArgs a) {
+  using L = DTile<D>;
+  constexpr int kCP = D + 4;                     // combine row: D values, max, sum, 16-byte pitch
+  constexpr int kComb = kWaves * 16 * kCP;      // floats of one head block's combine
+  constexpr int kSmemBytes =
+      (kWaves * L::wElems * 2 > kComb * 4) ? kWaves * L::wElems * 2 : kComb * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int unit = blockIdx.x;
+  const long long total = total_keys(a, lane);
+  const long long share = share_of(total, a.n_units);
+  const long long start = (long long)unit * share;
+  if (start >= total) return;  // uniform over the block
+  const long long end = min(start + share, total);
+
+  const int grp = lane >> 4;
+  const int i16 = lane & 15;
+  uint16_t* Kw = reinterpret_cast<uint16_t*>(smem) + wave * L::wElems;
+  uint16_t* Vw = Kw + L::kElems;
+  const int tr_row = 4 * grp + (i16 >> 2);
+  const int tr_col = 4 * (i16 & 3);
+
+  // cur: the piece being reduced (same on every wave). ld: the piece of the
+  // sub-block this wave has in flight (ld_pi its index, ld_sb its first key).
+  long long cur_pos = start;
+  Piece cur = locate(a, start, end - start, lane);
+  long long ld_pos = cur_pos;
+  Piece ld = cur;
+  int ld_pi = 0, ld_sb = cur.k0 + wave * kSub;
+  bool ld_ok = ld_sb < cur.k1 || next_sub(a, ld, ld_pos, end, ld_sb, ld_pi, wave);
+  if (ld_sb >= ld.k1) ld_ok = false;
+
+  u32x4 kr[L::kLoads], vr[L::kLoads];
+  if (ld_ok) load_sub<D>(a, ld, ld_sb, lane, kr, vr);
+  bf16x8 qf[HB][L::kDS];
+  float* comb = reinterpret_cast<float*>(smem);
+
+  for (int pi = 0;; ++pi) {
+    load_q<D, HB>(a, cur, grp, i16, qf);
+    f32x4 o[HB][D / 16];
+    float m_run[HB], l_run[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      m_run[hb] = -INFINITY;
+      l_run[hb] = 0.0f;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) o[hb][db] = f32x4{};
+    }
+    const int k1 = cur.k1;
+
+    // This wave's sub-blocks of the piece: keys k0 + 32*wave + 128*i.
+    while (ld_ok && ld_pi == pi) {
+#pragma unroll
+      for (int i = 0; i < L::kLoads; ++i) {
+        const int cidx = lane + 64 * i;
+        const int row = cidx / L::kCPR, col = (cidx % L::kCPR) * 8;
+        *reinterpret_cast<u32x4*>(Kw + row * L::kPitch + col) = kr[i];
+        *reinterpret_cast<u32x4*>(Vw + row * L::vPitch + col) = vr[i];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int cur_sb = ld_sb;
+      ld_ok = next_sub(a, ld, ld_pos, end, ld_sb, ld_pi, wave);
+      if (ld_ok) load_sub<D>(a, ld, ld_sb, lane, kr, vr);
+
+      // S^T[key][head]: lane holds keys cur_sb + 16kb + 4grp + i.
+      f32x4 s[HB][2];
+      {
+        bf16x8 kf[2][L::kDS];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int ds = 0; ds < L::kDS; ++ds)
+            kf[kb][ds] = *reinterpret_cast<const bf16x8*>(Kw + (16 * kb + i16) * L::kPitch + grp * (D / 4) + 8 * ds);
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            s[hb][kb] = f32x4{};
+#pragma unroll
+            for (int ds = 0; ds < L::kDS; ++ds) s[hb][kb] = mfma16x16x32(kf[kb][ds], qf[hb][ds], s[hb][kb]);
+          }
+      }
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (cur_sb + 16 * kb + 4 * grp + i >= k1) s[hb][kb][i] = -INFINITY;
+            mloc = fmaxf(mloc, s[hb][kb][i]);
+          }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        const float m_cand = mloc * a.c;
+        // Raise the reference max only when a score exceeds it by more than
+        // 2^kRescale; otherwise keep it (probabilities stay below 2^kRescale).
+        if (__any(m_cand > m_run[hb] + kRescale)) {
+          const float m_new = fmaxf(m_run[hb], m_cand);
+          const float alpha = fast_exp2(m_run[hb] - m_new);
+          m_run[hb] = m_new;
+          l_run[hb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 16; ++db) o[hb][db] = o[hb][db] * alpha;
+        }
+        float pv[8];
+        float psum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pv[j] = fast_exp2(fmaf(s[hb][j >> 2][j & 3], a.c, -m_run[hb]));
+          psum += pv[j];
+        }
+        l_run[hb] += psum;
+        const bf16x8 pf = pack_bf16x8(pv);
+        // Element j of pf is key 4grp + j (j < 4) or 16 + 4grp + j-4.
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+          const uint16_t* p0 = Vw + tr_row * L::vPitch + 16 * db + tr_col;
+          const bf16x8 vf = lds_read_tr_pair(p0, p0 + 16 * L::vPitch);
+          o[hb][db] = mfma16x16x32(vf, pf, o[hb][db]);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+
+    // Combine the 4 waves through LDS, one head block at a time; write the
+    // output rows when the piece is the whole stream, else a partial in slot 0
+    // (the share's first piece) or 1 (its last).
+    const bool whole = cur.k0 == 0 && k1 == cur.len;
+    const int slot = pi == 0 ? 0 : 1;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      float lsum = l_run[hb];
+      lsum += __shfl_xor(lsum, 16);
+      lsum += __shfl_xor(lsum, 32);
+      __syncthreads();  // LDS is free: staging buffers consumed, previous head block read
+      float* w = comb + (wave * 16 + i16) * kCP;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+        *reinterpret_cast<f32x4*>(w + 16 * db + 4 * grp) = o[hb][db];
+      if (grp == 0) {
+        w[D] = m_run[hb];
+        w[D + 1] = lsum;
+      }
+      __syncthreads();
+      for (int x = tid; x < 16 * D; x += kThreads) {
+        const int hh = x / D;
+        const int d = x - hh * D;
+        const int e = hb * 16 + hh;
+        if (e >= a.r) break;  // x only grows
+        float M = -INFINITY;
+#pragma unroll
+        for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, comb[(wv * 16 + hh) * kCP + D]);
+        float acc = 0.0f, den = 0.0f;
+#pragma unroll
+        for (int wv = 0; wv < kWaves; ++wv) {
+          const float* src = comb + (wv * 16 + hh) * kCP;
+          const float mw = src[D];
+          const float sc = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
+          acc += sc * src[d];
+          den += sc * src[D + 1];
+        }
+        if (whole) {
+          const size_t off = ((size_t)cur.b * a.h + cur.gam * a.r + e) * D + d;
+          const float y = acc / den;
+          if (a.out_bf16)
+            static_cast<uint16_t*>(a.out)[off] = static_cast<uint16_t>(pack_bf16x2(y, 0.0f) & 0xffffu);
+          else
+            static_cast<float*>(a.out)[off] = y;
+        } else {
+          const size_t prow = ((size_t)unit * 2 + slot) * a.r + e;
+          a.part_acc[prow * D + d] = acc;
+          if (d == 0) {
+            a.part_ml[prow * 2 + 0] = M;
+            a.part_ml[prow * 2 + 1] = den;
+          }
+        }
+      }
+    }
+    Piece n;
+    if (!next_piece(a, cur, cur_pos, end, n)) break;
+    cur = n;
+    __syncthreads();  // combine reads done before the staging buffers are rewritten
+  }
+}
+
+// One wave per (sequence, head): a stream cut over several shares has its
+// pieces merged by log-sum-exp; a sequence with no cached keys gets a zero
+// row. Streams that lie in one share were written by decode_kernel.
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(KArgs a) {
-  const int row = blockIdx.x;  // b*h + head
+__global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);  // b * h + head
+  if (row >= a.B * a.h) return;
   const int b = row / a.h;
-  const int len = min(max(a.lens[b], 0), a.T_max);
-  const int n_valid = div_up(len, a.chunk);
-  const int lane = threadIdx.x;
+  const int head = row - b * a.h;
+  const int gam = head / a.r;
+  const int e = head - gam * a.r;
   constexpr int EPL = D / 64;
+  // Global position of the stream, g * (keys of sequences before b) + gam *
+  // len, and the total, from one pass over lens.
+  long long before = 0, total = 0;
+  for (int bb = lane; bb < a.B; bb += 64) {
+    const long long l = seq_len(a, bb);
+    total += l;
+    before += bb < b ? l : 0;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    before += __shfl_xor(before, o);
+    total += __shfl_xor(total, o);
+  }
+  const int len = seq_len(a, b);
+  if (len == 0) {
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) {
+      const size_t off = (size_t)row * D + lane + 64 * x;
+      if (a.out_bf16)
+        static_cast<uint16_t*>(a.out)[off] = 0;
+      else
+        static_cast<float*>(a.out)[off] = 0.0f;
+    }
+    return;
+  }
+  total *= a.g;
+  const long long share = share_of(total, a.n_units);
+  const long long start = before * a.g + (long long)gam * len;
+  const int u0 = (int)(start / share);
+  const int u1 = (int)((start + len - 1) / share);
+  if (u0 == u1) return;
+  // The first piece sits in slot 1 of unit u0 when that share began in an
+  // earlier stream, else in slot 0; every later piece is its unit's first.
+  const int slot0 = (long long)u0 * share < start ? 1 : 0;
+  const int n = u1 - u0 + 1;
+  auto prow_of = [&](int j) {
+    return ((size_t)(u0 + j) * 2 + (j == 0 ? slot0 : 0)) * a.r + e;
+  };
+  // Pieces in rounds of 64: lane j holds piece j's (max, sum); the
+  // accumulator loads do not depend on the max, so a round issues together.
+  float M = -INFINITY, den = 0.0f;
   float acc[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-  float M = -INFINITY;
-  for (int s = 0; s < n_valid; ++s) M = fmaxf(M, a.part_ml[((size_t)row * a.n_split + s) * 2]);
-  float den = 0.0f;
-  for (int s = 0; s < n_valid; ++s) {
-    const size_t pidx = (size_t)row * a.n_split + s;
-    const float sc = fast_exp2(a.part_ml[pidx * 2] - M);
-    den += sc * a.part_ml[pidx * 2 + 1];
+  for (int x = 0; x < EPL; ++x) acc[x] = 0.0f;
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    const int nj = min(64, n - j0);
+    float mj = -INFINITY, lj = 0.0f;
+    if (lane < nj) {
+      const size_t pr = prow_of(j0 + lane);
+      mj = a.part_ml[pr * 2];
+      lj = a.part_ml[pr * 2 + 1];
+    }
+    float Mr = mj;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += sc * a.part_acc[pidx * D + lane + 64 * e];
+    for (int o = 32; o >= 1; o >>= 1) Mr = fmaxf(Mr, __shfl_xor(Mr, o));
+    const float Mn = fmaxf(M, Mr);
+    const float alpha = M == -INFINITY ? 0.0f : fast_exp2(M - Mn);
+    float dj = lane < nj ? fast_exp2(mj - Mn) * lj : 0.0f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) dj += __shfl_xor(dj, o);
+    den = den * alpha + dj;
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) acc[x] *= alpha;
+#pragma unroll 4
+    for (int j = 0; j < nj; ++j) {
+      const float sc = fast_exp2(__shfl(mj, j) - Mn);
+      const size_t pr = prow_of(j0 + j);
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) acc[x] += sc * a.part_acc[pr * D + lane + 64 * x];
+    }
+    M = Mn;
   }
-  const float inv = n_valid > 0 ? 1.0f / den : 0.0f;
+  const float inv = 1.0f / den;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const float y = acc[e] * inv;
-    const size_t off = (size_t)row * D + lane + 64 * e;
+  for (int x = 0; x < EPL; ++x) {
+    const float y = acc[x] * inv;
+    const size_t off = (size_t)row * D + lane + 64 * x;
     if (a.out_bf16)
       static_cast<uint16_t*>(a.out)[off] = static_cast<uint16_t>(pack_bf16x2(y, 0.0f) & 0xffffu);
     else
       static_cast<float*>(a.out)[off] = y;
   }
+}
+
+template <int D, int HB>
+const void* kernel_ptr() {
+  return reinterpret_cast<const void*>(&decode_kernel<D, HB>);
+}
+
+template <int D>
+const void* kernel_for_hb(int hb) {
+  if (hb == 1) return kernel_ptr<D, 1>();
+  if (hb == 2) return kernel_ptr<D, 2>();
+  if (hb <= 4) return kernel_ptr<D, 4>();
+  return nullptr;
+}
+
+const void* decode_kernel_for(int d, int hb) {
+  if (d == 64) return kernel_for_hb<64>(hb);
+  if (d == 128) return kernel_for_hb<128>(hb);
+  return nullptr;
 }
 
 template <int D>
@@ -316,57 +534,41 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   a.out = p.out;
   a.part_acc = p.part_acc;
   a.part_ml = p.part_ml;
+  a.B = p.B;
   a.h = p.h;
   a.g = p.g;
   a.r = p.h / p.g;
   a.T_max = p.T_max;
-  a.chunk = p.chunk;
-  a.n_split = p.n_split;
+  a.n_units = p.n_units;
   a.c = p.scale * kLog2e;
   a.out_bf16 = p.out_bf16;
-  const dim3 grid(p.B * p.g * p.n_split), block(kThreads);
+  const dim3 grid(p.n_units), block(kThreads);
   const int hb = div_up(a.r, 16);
   if (hb == 1)
-    hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, 1>), grid, block, 0, stream, a);
   else if (hb == 2)
-    hipLaunchKernelGGL((decode_split_kernel<D, 2>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, 2>), grid, block, 0, stream, a);
   else if (hb <= 4)
-    hipLaunchKernelGGL((decode_split_kernel<D, 4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, 4>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.n_split == 1) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(p.B * p.h), dim3(64), 0, stream, a);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(div_up(p.B * p.h, kWaves)), block, 0, stream, a);
   return hipGetLastError();
-}
-
-template <int D>
-const void* kernel_for_hb(int hb) {
-  if (hb == 1) return reinterpret_cast<const void*>(&decode_split_kernel<D, 1>);
-  if (hb == 2) return reinterpret_cast<const void*>(&decode_split_kernel<D, 2>);
-  if (hb <= 4) return reinterpret_cast<const void*>(&decode_split_kernel<D, 4>);
-  return nullptr;
-}
-
-const void* decode_kernel_for(int d, int hb) {
-  if (d == 64) return kernel_for_hb<64>(hb);
-  if (d == 128) return kernel_for_hb<128>(hb);
-  return nullptr;
 }
 
 }  // namespace
 
 bool decode_supports(int d) { return d == 64 || d == 128; }
 
-int decode_chunk(int B, int h, int g, int T_max, int d) {
-  if (const char* env = std::getenv("GQA_DECODE_CHUNK")) {
-    const int c = std::atoi(env);
-    if (c > 0) return div_up(c, 128) * 128;
+int decode_units(int h, int g, int d) {
+  if (const char* env = std::getenv("GQA_DECODE_UNITS")) {
+    const int u = std::atoi(env);
+    if (u > 0) return u;
   }
-  // Few, long key streams: a block streams its chunk with one 32-key
-  // sub-block per wave in flight, and per-chunk costs (first-load latency,
-  // the block combine, the partial write and the merge) favour long chunks.
-  // Split only as far as needed to give every block slot of the chip work.
+  // One workgroup per resident workgroup slot of the chip: every share is
+  // streamed concurrently and they all end together.
   int n_cu = 256, per_cu = 2;
   int dev = 0;
   if (hipGetDevice(&dev) == hipSuccess) {
@@ -379,11 +581,7 @@ int decode_chunk(int B, int h, int g, int T_max, int d) {
       per_cu = blocks;
   }
   (void)hipGetLastError();
-  const long long streams = (long long)B * g;
-  const long long want = (long long)per_cu * n_cu;
-  const int n_split = streams >= want ? 1 : (int)((want + streams - 1) / streams);
-  const int c = div_up(div_up(T_max, n_split), 128) * 128;
-  return c > 0 ? c : 128;
+  return n_cu * per_cu;
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {

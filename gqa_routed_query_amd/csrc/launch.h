@@ -42,11 +42,10 @@ struct DecodeParams {
   const void* v_cache;  // [B, g, T_max, d] bf16
   const int32_t* lens;  // [B] on the device
   void* out;            // [B, h, d]
-  float* part_acc;      // [B*h, n_split, d] fp32 workspace
-  float* part_ml;       // [B*h, n_split, 2] fp32 workspace
+  float* part_acc;      // [n_units, 2, h/g, d] fp32 workspace
+  float* part_ml;       // [n_units, 2, h/g, 2] fp32 workspace
   int B, h, g, T_max, d;
-  int chunk;            // keys per split (multiple of 128)
-  int n_split;          // ceil(T_max / chunk)
+  int n_units;          // waves that share the key range
   float scale;
   int out_bf16;
 };
@@ -61,7 +60,7 @@ bool attn_bf16_supports(int d);
 bool attn_f32_supports(int d);
 bool decode_supports(int d);
 
-// Decode split size in keys for a problem shape (honours GQA_DECODE_CHUNK).
-int decode_chunk(int B, int h, int g, int T_max, int d);
+// Waves that share a decode call's key range (honours GQA_DECODE_UNITS).
+int decode_units(int h, int g, int d);
 
 }  // namespace gqa

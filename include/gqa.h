@@ -84,9 +84,12 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, void* out,
                        float scale, int causal, void* stream);
 
 /*
- * Bytes of device workspace gqa_decode needs for this shape (0 when the
- * cache fits one split). Depends only on the arguments (and on the
- * GQA_DECODE_CHUNK environment variable, which overrides the split size).
+ * Bytes of device workspace gqa_decode needs: two partial results (h/g heads
+ * of d fp32 values plus a max and a sum each) per wave of the decode grid,
+ * which holds one wave per resident wave slot of the current device. It does
+ * not depend on B or T_max (they are accepted for the shape check only);
+ * 0 for an invalid shape. The GQA_DECODE_UNITS environment variable overrides
+ * the wave count.
  */
 size_t gqa_decode_workspace_bytes(int B, int h, int g, int T_max, int d);
 
@@ -100,7 +103,8 @@ size_t gqa_decode_workspace_bytes(int B, int h, int g, int T_max, int d);
  *           >= lens[b] are never read (they may hold anything, NaN included).
  *   out     [B, h, d] out_dtype; lens[b] = 0 gives a zero row.
  *   workspace: device memory of at least gqa_decode_workspace_bytes(...)
- *           bytes (may be NULL when that is 0); contents are scratch.
+ *           bytes, 16-byte aligned; contents are scratch (no zeroing needed).
+ *           Calls that overlap on one workspace race.
  * Supported: in_dtype BF16, d in {64, 128}, h/g <= 64.
  * Returns GQA_ERR_WORKSPACE when workspace_bytes is too small.
  */

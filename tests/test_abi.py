@@ -138,11 +138,20 @@ def test_kv_cache_bytes_matches_oracle_law():
 
 def test_decode_workspace_bytes():
     assert gq.gqa_decode_workspace_bytes(0, 8, 2, 100, 128) == 0
-    # one split: no workspace
-    assert gq.gqa_decode_workspace_bytes(1, 8, 2, 100, 128) == 0
-    # 512 KV streams fill the chip without splitting: no partials
-    assert gq.gqa_decode_workspace_bytes(64, 32, 8, 8192, 128) == 0
-    # few long streams are split; partials stay a small fraction of the cache
-    big = gq.gqa_decode_workspace_bytes(2, 8, 2, 16384, 128)
-    assert big > 0
-    assert big < 0.05 * gq.gqa_kv_cache_bytes(2, 2, 16384, 128)
+    assert gq.gqa_decode_workspace_bytes(2, 8, 3, 100, 128) == 0   # g does not divide h
+    # two partials of r heads per wave of the grid: independent of B and T_max
+    small = gq.gqa_decode_workspace_bytes(1, 8, 2, 100, 128)
+    assert small > 0
+    assert small == gq.gqa_decode_workspace_bytes(64, 8, 2, 16384, 128)
+    # and proportional to r*(d+2) (up to the 256-byte alignment of the first region)
+    r4 = gq.gqa_decode_workspace_bytes(64, 32, 8, 8192, 128)
+    r1 = gq.gqa_decode_workspace_bytes(64, 32, 32, 8192, 128)
+    assert abs(r4 - 4 * r1) <= 1024
+    # a small fraction of the decode workload's cache (64 x 8 groups x 8192 keys)
+    assert r4 < 0.01 * gq.gqa_kv_cache_bytes(64, 8, 8192, 128)
+
+
+def test_decode_workspace_units_override(monkeypatch):
+    monkeypatch.setenv("GQA_DECODE_UNITS", "3")
+    # 3 waves x 2 partials x 4 heads x 128 floats (rounded to 256 B) + 3 x 2 x 4 x 2 floats
+    assert gq.gqa_decode_workspace_bytes(4, 16, 4, 1000, 128) == 12288 + 192

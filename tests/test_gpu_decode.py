@@ -62,17 +62,44 @@ def test_decode_edge_lengths():
 
 
 def test_decode_split_invariance(monkeypatch):
-    """The result does not depend on the split size (up to fp32 rounding)."""
-    q, kc, vc, lens = decode_inputs(4, 16, 4, 3000, 128, (1, 3000), seed=41)
+    """The result does not depend on how the key range is shared out over
+    waves (up to fp32 rounding): one wave (every stream whole), a few waves
+    (streams cut into long pieces), many waves (short pieces, several per
+    stream) and the default grid."""
+    q, kc, vc, lens = decode_inputs(6, 16, 4, 3000, 128, (1, 3000), seed=41)
+    lens[2] = 0
     outs = []
-    for chunk in ("128", "512", "4096"):
-        say(f"decode split chunk={chunk}")
-        monkeypatch.setenv("GQA_DECODE_CHUNK", chunk)
+    for units in ("1", "3", "64", "1000", None):
+        say(f"decode units={units}")
+        if units:
+            monkeypatch.setenv("GQA_DECODE_UNITS", units)
+        else:
+            monkeypatch.delenv("GQA_DECODE_UNITS", raising=False)
         outs.append(_run(q, kc, vc, lens))
-    monkeypatch.delenv("GQA_DECODE_CHUNK")
-    assert max_abs(outs[0], outs[1]) <= 1e-3
-    assert max_abs(outs[0], outs[2]) <= 1e-3
-    assert max_abs(outs[0], oracle.gqa_decode_ref(q, kc, vc, lens)) <= TOL_BF16
+    ref = oracle.gqa_decode_ref(q, kc, vc, lens)
+    for o in outs:
+        assert float(o[2].abs().max()) == 0.0
+        assert max_abs(o, outs[0]) <= 1e-3
+        assert max_abs(o, ref) <= TOL_BF16
+
+
+def test_decode_repeated_calls_reuse_workspace():
+    """Back-to-back calls with different lengths on one workspace give the
+    same result as fresh calls: partial slots are rewritten each call and
+    need no clearing."""
+    import gqa_routed_query_amd as gq
+
+    d = dev()
+    q, kc, vc, lens = decode_inputs(8, 16, 4, 2048, 128, (1, 2048), seed=43)
+    q, kc, vc = q.to(d), kc.to(d), vc.to(d)
+    ws = torch.full((gq.gqa_decode_workspace_bytes(8, 16, 4, 2048, 128),), 0x7f, dtype=torch.uint8,
+                    device=d)
+    say("decode workspace reuse")
+    for seed_lens in ([2048] * 8, [5, 2048, 0, 700, 33, 1500, 64, 1]):
+        ln = torch.tensor(seed_lens, dtype=torch.int32)
+        out = gq.gqa_decode(q, kc, vc, ln.to(d), out_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        assert max_abs(out, oracle.gqa_decode_ref(q.cpu(), kc.cpu(), vc.cpu(), ln)) <= TOL_BF16
 
 
 def test_decode_matches_prefill_last_row():
