@@ -484,7 +484,6 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
     den = den * alpha + dj;
 #pragma unroll
     for (int x = 0; x < EPL; ++x) acc[x] *= alpha;
-#pragma unroll 4
     for (int j = 0; j < nj; ++j) {
       const float sc = fast_exp2(__shfl(mj, j) - Mn);
       const size_t pr = prow_of(j0 + j);
