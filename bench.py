@@ -54,7 +54,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-sweep", action="store_true", help="skip the KV-group decode sweep")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the sweeps outside the step (KV-group decode, GQE vs GQA over T)")
     ap.add_argument("--only", choices=["prefill", "decode", "gqe", "copy"], default=None,
                     help="profile helper: run only one kernel family (copy = calibration copy)")
     return ap.parse_args()
@@ -110,7 +111,7 @@ def main():
     import torch
 
     import gqa_routed_query_amd as gq
-    from workloads import WORKLOADS, decode_inputs, gqe_inputs, prefill_inputs
+    from workloads import WORKLOADS, decode_inputs, gqe_inputs, gqe_sweep_points, prefill_inputs
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -246,6 +247,42 @@ def main():
             del q, kc, vc, out, wsb
             torch.cuda.empty_cache()
 
+    # ---- GQE vs dense GQA over the sequence length, outside the step ----
+    gsweep = []
+    if run_gqe and not args.no_sweep:
+        if run_prefill:
+            del pout
+        del gq_, gk, gv, glg, gout
+        torch.cuda.empty_cache()
+        for (B, h, g, T, d, ks, seed) in gqe_sweep_points():
+            q, k, v, lg = gqe_inputs(B, h, g, T, d, "bf16", seed=seed, device=dev)
+            out = torch.empty_like(q)
+            dense_flops = 2.0 * B * h * d * T * (T + 1)
+
+            def timed(fn, n_warm=2, n=5):
+                tm = Timer(torch)
+                for it in range(n_warm + n):
+                    if it < n_warm:
+                        fn()
+                        continue
+                    with tm:
+                        fn()
+                torch.cuda.synchronize()
+                return stats(tm.ms())["median_ms"]
+
+            dense_ms = timed(lambda: gq.gqa_prefill(q, k, v, causal=True, out=out))
+            for kk in ks:
+                ms = timed(lambda: gq.gqe_routed_prefill(q, k, v, lg, kk, causal=True, out=out))
+                fl = dense_flops * kk / (h // g)
+                gsweep.append(dict(B=B, h=h, g=g, T=T, d=d, top_k=kk, routed_us=ms * 1e3,
+                                   dense_us=dense_ms * 1e3, speedup=dense_ms / ms,
+                                   routed_tflops=fl / (ms * 1e-3) / 1e12,
+                                   dense_tflops=dense_flops / (dense_ms * 1e-3) / 1e12))
+                log(f"gqe sweep h={h} g={g} T={T} B={B} k={kk}: routed {ms*1e3:.1f} us, "
+                    f"dense {dense_ms*1e3:.1f} us, speed-up {dense_ms/ms:.2f}")
+            del q, k, v, lg, out
+            torch.cuda.empty_cache()
+
     # ---- CPU oracle baseline on a bounded sample of the prefill workload ----
     cpu = None
     if run_prefill and not args.no_cpu:
@@ -300,6 +337,8 @@ def main():
         line["gqe"]["dense_gqa_same_shape_us"] = dense_same["mean_ms"] * 1e3
     if sweep:
         line["decode_sweep"] = sweep
+    if gsweep:
+        line["gqe_sweep"] = gsweep
     if cpu:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -204,18 +204,17 @@ def gqe_topk_ref(logits, g: int, top_k: int):
     r = h // g
     if h % g or not 1 <= top_k <= r:
         raise ValueError("need g | h and 1 <= top_k <= h/g")
-    idx = np.empty((B, T, g, top_k), dtype=np.int32)
-    gate = np.empty((B, T, g, top_k))
-    for b in range(B):
-        for t in range(T):
-            for gam in range(g):
-                ell = lg[b, t, gam * r:(gam + 1) * r]
-                order = sorted(range(r), key=lambda e: (-ell[e], e))
-                sel = order[:top_k]
-                prob = softmax(ell)
-                w = prob[sel] / prob[sel].sum()
-                idx[b, t, gam] = [gam * r + e for e in sel]
-                gate[b, t, gam] = w
+    ell = lg.reshape(B, T, g, r)                       # the group's r expert logits
+    expert = np.broadcast_to(np.arange(r), ell.shape)
+    # Rank order: sort by the key (-logit, expert); np.lexsort takes the primary
+    # key last. -0.0 and +0.0 compare equal, so they tie and go by expert index.
+    order = np.lexsort((expert, -ell), axis=-1)
+    sel = order[..., :top_k]                           # [B,T,g,k] experts in rank order
+    prob = np.exp(ell - ell.max(axis=-1, keepdims=True))
+    prob /= prob.sum(axis=-1, keepdims=True)           # router probabilities in the group
+    kept = np.take_along_axis(prob, sel, axis=-1)
+    gate = kept / kept.sum(axis=-1, keepdims=True)     # renormalised over the kept
+    idx = (sel + (np.arange(g) * r)[None, None, :, None]).astype(np.int32)
     return idx, gate
 
 

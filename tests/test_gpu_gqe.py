@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from gpu_util import TOL_BF16, TOL_F32, TOL_GATE, dev, max_abs, np64, sample_tokens, say
-from workloads import WORKLOADS, gqe_inputs, prefill_inputs
+from workloads import WORKLOADS, gqe_inputs, gqe_sweep_points, prefill_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -90,3 +90,47 @@ def test_gqe_headline_shape(top_k):
                     ref = rgate[b, t, gam, j] * oracle.gqa_ref_row(qc, kc, vc, b, i, t)
                     worst = max(worst, float(np.abs(np64(oc[b, i, t]) - ref).max()))
     assert worst <= TOL_BF16, worst
+
+
+@pytest.mark.parametrize("B,h,g,T,d,ks,seed", gqe_sweep_points(),
+                         ids=lambda x: str(x) if not isinstance(x, tuple) else "k" + "".join(map(str, x)))
+def test_gqe_sweep_point(B, h, g, T, d, ks, seed):
+    """The GQE-vs-GQA sequence-length sweep (2k .. 64k tokens per sequence):
+    for each k, all router indices bit-exact, gates within 1e-6, a row is
+    nonzero iff its head was kept, and sampled kept rows equal gate x the
+    oracle's dense row; the dense GQA output the sweep compares against is
+    checked on sampled rows as well."""
+    import gqa_routed_query_amd as gq
+
+    dv = dev()
+    say(f"gqe sweep B={B} h={h} g={g} T={T} k={ks}")
+    q, k, v, lg = gqe_inputs(B, h, g, T, d, "bf16", seed=seed, device=dv)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    toks = sample_tokens(T, 6, seed=seed)
+    for top_k in ks:
+        out, idx, gate = _run(q, k, v, lg, top_k, out_dtype=torch.bfloat16)
+        ridx, rgate = oracle.gqe_topk_ref(lg.cpu(), g, top_k)
+        assert np.array_equal(idx.cpu().numpy(), ridx)
+        assert max_abs(gate, rgate) <= TOL_GATE
+        kept = torch.zeros(B, T, h, dtype=torch.bool, device=dv)
+        kept.scatter_(2, idx.view(B, T, -1).long(), True)
+        assert torch.equal((out != 0).any(-1).permute(0, 2, 1), kept)
+        worst = 0.0
+        for t in toks:
+            for bb in {0, B - 1}:
+                for gam in (0, g - 1):
+                    for j in range(top_k):
+                        i = int(ridx[bb, t, gam, j])
+                        ref = rgate[bb, t, gam, j] * oracle.gqa_ref_row(qc, kc, vc, bb, i, t)
+                        worst = max(worst, float(np.abs(np64(out[bb, i, t]) - ref).max()))
+        assert worst <= TOL_BF16, (top_k, worst)
+        del out, idx, gate, kept
+    dense = gq.gqa_prefill(q, k, v, causal=True, out_dtype=torch.bfloat16)
+    worst = 0.0
+    for t in toks:
+        for i in (0, h // 2, h - 1):
+            ref = oracle.gqa_ref_row(qc, kc, vc, B - 1, i, t)
+            worst = max(worst, float(np.abs(np64(dense[B - 1, i, t]) - ref).max()))
+    assert worst <= TOL_BF16, worst
+    del q, k, v, lg, dense
+    torch.cuda.empty_cache()

@@ -28,6 +28,8 @@ __all__ = [
     "router_logits",
     "gqe_inputs",
     "torch_dtype",
+    "GQE_SWEEP_T",
+    "gqe_sweep_points",
 ]
 
 
@@ -69,6 +71,28 @@ WORKLOADS = {
     "gqe": Workload("gqe", "gqe", B=2, h=32, g=8, T=4096, d=128, dtype="bf16",
                     seed=5, top_k=(1, 2)),
 }
+
+# GQE-vs-GQA speed-up over the sequence length: the pages report the routed
+# model's speed-up for 2k to 1024k-token sequences (gist.science GQE explainer,
+# section "Resultats Experimentaux"). Every point holds GQE_SWEEP_TOKENS tokens
+# (B = tokens / T, at least 1) so short sequences still fill the chip. Head
+# shapes: the pages' 16 query heads over 8 KV groups with k = 1, and the
+# 32-head / 8-group shape of the GQE workload with k = 1 and 2.
+GQE_SWEEP_T = (2048, 4096, 8192, 16384, 32768, 65536)
+GQE_SWEEP_TOKENS = 32768
+GQE_SWEEP_SHAPES = ((16, 8, (1,)), (32, 8, (1, 2)))  # (h, g, top_k values)
+GQE_SWEEP_D = 128
+GQE_SWEEP_SEED = 6
+
+
+def gqe_sweep_points():
+    """(B, h, g, T, d, top_k values, seed) for every point of the sweep."""
+    pts = []
+    for h, g, ks in GQE_SWEEP_SHAPES:
+        for T in GQE_SWEEP_T:
+            B = max(1, GQE_SWEEP_TOKENS // T)
+            pts.append((B, h, g, T, GQE_SWEEP_D, ks, GQE_SWEEP_SEED + T + h))
+    return pts
 
 
 def _gen(seed: int, device: str | torch.device) -> torch.Generator:
