@@ -52,6 +52,7 @@ __all__ = [
     "gqa_decode_ref",
     "gqe_topk_ref",
     "gqe_ref",
+    "gqe_decode_ref",
     "kv_cache_bytes",
     "gqe_active_query_heads",
 ]
@@ -237,6 +238,34 @@ def gqe_ref(q, k, v, logits, top_k: int, causal: bool = True,
                 for j in range(top_k):
                     i = int(idx[b, t, gam, j])
                     out[b, i, t] = gate[b, t, gam, j] * dense[b, i, t]
+    return out, idx, gate
+
+
+def gqe_decode_ref(q, k_cache, v_cache, lens, logits, top_k: int,
+                   scale: float | None = None):
+    """GQE routed decode step -> (out [B,h,d] float64, idx [B,g,k], gate [B,g,k]).
+
+    One new token per sequence. The router keeps top_k of the h/g query-head
+    experts of every KV group for that token (gist.science GQE explainer,
+    section "Architecture et Routage"); the K/V cache stays dense, so a kept
+    head attends to every cached position below lens[b] of its group exactly
+    as in plain decode, and its row is multiplied by its gate. Rows of heads
+    the router did not keep are 0, and so is every row of a sequence with no
+    cached keys. logits [B,h] holds the router's score of every head for the
+    new token.
+    """
+    q = _f64(q)
+    B, h, d = q.shape
+    g = k_cache.shape[1]
+    idx, gate = gqe_topk_ref(_f64(logits).reshape(B, 1, h), g, top_k)
+    idx, gate = idx[:, 0], gate[:, 0]                  # [B,g,k]
+    dense = gqa_decode_ref(q, k_cache, v_cache, lens, scale)
+    out = np.zeros_like(dense)
+    for b in range(B):
+        for gam in range(g):
+            for j in range(top_k):
+                i = int(idx[b, gam, j])
+                out[b, i] = gate[b, gam, j] * dense[b, i]
     return out, idx, gate
 
 

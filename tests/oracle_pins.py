@@ -341,6 +341,44 @@ def pin_gqe_structure():
     assert np.abs(outp - out[:, perm]).max() < 1e-12
 
 
+def pin_gqe_decode():
+    """Routed decode of token t over a cache of positions 0..t, with token t's
+    router logits, equals row t of routed prefill (same kept heads, gates and
+    rows); k = h/g keeps every head with gates equal to the group softmax
+    (scipy); a sequence with no cached keys gives zero rows; NaN padding past
+    lens is never read."""
+    B, h, g, T, d = 3, 8, 2, 12, 8
+    r = h // g
+    q = _rand((B, h, T, d), 190)
+    k = _rand((B, g, T, d), 191)
+    v = _rand((B, g, T, d), 192)
+    lg = _tied_logits((B, T, h), 193).astype(np.float32)
+    ts = [0, 5, 11]
+    lens = np.array([t + 1 for t in ts])
+    qd = np.stack([q[b, :, t] for b, t in enumerate(ts)])
+    lgd = np.stack([lg[b, t] for b, t in enumerate(ts)])
+    kc, vc = k.copy(), v.copy()
+    for b, n in enumerate(lens):
+        kc[b, :, n:] = np.nan
+        vc[b, :, n:] = np.nan
+    for kk in (1, 2, r):
+        pre, pidx, pgate = orc.gqe_ref(q, k, v, lg, kk, causal=True)
+        out, idx, gate = orc.gqe_decode_ref(qd, kc, vc, lens, lgd, kk)
+        assert np.isfinite(out).all()
+        for b, t in enumerate(ts):
+            assert np.array_equal(idx[b], pidx[b, t])
+            assert np.abs(gate[b] - pgate[b, t]).max() < 1e-15
+            assert np.abs(out[b] - pre[b, :, t]).max() < 1e-12, (kk, t)
+        assert (np.abs(out).sum(-1) > 0).sum() == B * g * kk
+    out, idx, gate = orc.gqe_decode_ref(qd, kc, vc, lens, lgd, r)
+    for b in range(B):
+        for gam in range(g):
+            sm = scipy.special.softmax(lgd[b, gam * r:(gam + 1) * r].astype(np.float64))
+            assert np.abs(gate[b, gam] - sm[idx[b, gam] - gam * r]).max() < 1e-14
+    out0, _, _ = orc.gqe_decode_ref(qd, kc, vc, np.array([0, 4, 0]), lgd, 2)
+    assert np.all(out0[0] == 0) and np.all(out0[2] == 0) and np.abs(out0[1]).sum() > 0
+
+
 # --------------------------------------------------------------------------
 # Accounting printed on the pages
 # --------------------------------------------------------------------------
@@ -385,6 +423,7 @@ PINS = [
     pin_topk_stable_argsort,
     pin_gates,
     pin_gqe_structure,
+    pin_gqe_decode,
     pin_kv_cache_law,
     pin_gqe_active_count,
 ]

@@ -98,6 +98,18 @@ def _kv_head_strided(i, h, g):
     return i % g
 
 
+def _gqe_decode_no_gate(q, kc, vc, lens, logits, top_k, scale=None):
+    out, idx, gate = _orig["gqe_decode_ref"](q, kc, vc, lens, logits, top_k, scale)
+    dense = _orig["gqa_decode_ref"](q, kc, vc, lens, scale)
+    return np.where(np.abs(out).sum(-1, keepdims=True) > 0, dense, 0.0), idx, gate
+
+
+def _gqe_decode_no_zero(q, kc, vc, lens, logits, top_k, scale=None):
+    out, idx, gate = _orig["gqe_decode_ref"](q, kc, vc, lens, logits, top_k, scale)
+    dense = _orig["gqa_decode_ref"](q, kc, vc, lens, scale)
+    return np.where(np.abs(out).sum(-1, keepdims=True) > 0, out, dense), idx, gate
+
+
 def _active_no_shared(g, top_k, shared=1):
     return g * top_k
 
@@ -117,6 +129,8 @@ MUTATIONS = {
     "topk/gate_unrenormalised": ("gqe_topk_ref", _topk_gate_unrenormalised),
     "gqe/unselected_not_zero": ("gqe_ref", _gqe_no_zero),
     "gqe/gate_dropped": ("gqe_ref", _gqe_no_gate),
+    "gqe_decode/gate_dropped": ("gqe_decode_ref", _gqe_decode_no_gate),
+    "gqe_decode/unselected_not_zero": ("gqe_decode_ref", _gqe_decode_no_zero),
     "kv_cache_bytes/no_factor_two": ("kv_cache_bytes", _kv_bytes_no_two),
     "kv_head_of/strided": ("kv_head_of", _kv_head_strided),
     "active_heads/no_shared": ("gqe_active_query_heads", _active_no_shared),
