@@ -111,7 +111,8 @@ def main():
     import torch
 
     import gqa_routed_query_amd as gq
-    from workloads import WORKLOADS, decode_inputs, gqe_inputs, gqe_sweep_points, prefill_inputs
+    from workloads import (WORKLOADS, decode_inputs, gqe_inputs, gqe_sweep_points, prefill_inputs,
+                           router_logits)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -215,6 +216,31 @@ def main():
                                           flops_per_call=fl,
                                           speedup_vs_dense=dense_same["mean_ms"] / sg["mean_ms"])
             log(f"gqe k={kk}: {sg['mean_ms']*1e3:.1f} us/call, {tf:.1f} TFLOP/s")
+
+    # ---- GQE routed decode at the decode workload, outside the step ----
+    gdec = {}
+    if run_decode and not args.no_sweep:
+        dlg = router_logits(wd.B, 1, wd.h, seed=wd.seed + 100, device=dev)[:, 0].contiguous()
+        for kk in (1, 2):
+            tm = Timer(torch)
+            for it in range(3 + args.steps):
+                flush.sum()
+                if it < 3:
+                    gq.gqe_routed_decode(dq, dk, dv, dlens, dlg, kk, out=dout, workspace=dws)
+                    continue
+                with tm:
+                    gq.gqe_routed_decode(dq, dk, dv, dlens, dlg, kk, out=dout, workspace=dws)
+            torch.cuda.synchronize()
+            sg = stats(tm.ms())
+            # the K/V stream is the same as plain decode; only the kept heads'
+            # queries are read; every output row is written; logits, idx, gates
+            nb = (2 * wd.g * wd.d * 2) * sum_lens + wd.B * wd.g * kk * wd.d * 2 + dq.numel() * 2 \
+                + dlg.numel() * 4 + 2 * wd.B * wd.g * kk * 4
+            gdec[f"top{kk}"] = dict(mean_us=sg["mean_ms"] * 1e3, GBps=nb / (sg["mean_ms"] * 1e-3) / 1e9,
+                                    frac=nb / (sg["mean_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                                    time_vs_dense_decode=sg["mean_ms"] / res["decode"]["mean_ms"])
+            log(f"gqe decode k={kk}: {sg['mean_ms']*1e3:.1f} us/call, {gdec[f'top{kk}']['GBps']:.0f} GB/s")
+        del dlg
 
     # ---- KV-group sweep (decode), outside the step ----
     sweep = []
@@ -339,6 +365,8 @@ def main():
         line["decode_sweep"] = sweep
     if gsweep:
         line["gqe_sweep"] = gsweep
+    if gdec:
+        line["gqe_decode"] = gdec
     if cpu:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -8,6 +8,7 @@ this package only marshals torch tensors into its entry points:
 * :func:`gqa_decode` -- one decode step over a KV cache [B,g,T_max,d].
 * :func:`gqe_routed_prefill` -- GQE: top-k query-head experts per KV group
   per token, dense K/V.
+* :func:`gqe_routed_decode` -- GQE routing applied to one decode step.
 
 torch provides device memory and the stream; every step of the computation
 runs in the library's kernels. Importing the package fails loudly when the
@@ -22,6 +23,7 @@ from ._binding import (  # noqa: F401
     gqa_decode_workspace_bytes,
     gqa_kv_cache_bytes,
     gqa_prefill,
+    gqe_routed_decode,
     gqe_routed_prefill,
     last_error,
     lib_path,

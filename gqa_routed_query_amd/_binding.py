@@ -50,6 +50,9 @@ def _load():
     lib.gqe_routed_prefill.restype = i32
     lib.gqe_routed_prefill.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32,
                                        i32, i32, i32, f32, i32, vp]
+    lib.gqe_routed_decode.restype = i32
+    lib.gqe_routed_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32,
+                                      i32, i32, i32, f32, vp, sz, vp]
     lib.gqa_kv_cache_bytes.restype = ctypes.c_uint64
     lib.gqa_kv_cache_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.gqa_status_string.restype = ctypes.c_char_p
@@ -124,7 +127,7 @@ def gqa_prefill(q, k, v, causal: bool = True, scale: float | None = None, out=No
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share one dtype")
     g = k.shape[1]
-    out_dtype = out_dtype or q.dtype
+    out_dtype = out_dtype or (out.dtype if out is not None else q.dtype)
     if out is None:
         out = torch.empty((B, h, T, d), dtype=out_dtype, device=dev)
     elif out.shape != q.shape or out.dtype != out_dtype:
@@ -152,7 +155,7 @@ def gqa_decode(q, k_cache, v_cache, lens, scale: float | None = None, out=None,
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q and the caches must share one dtype")
     g, T_max = k_cache.shape[1], k_cache.shape[2]
-    out_dtype = out_dtype or q.dtype
+    out_dtype = out_dtype or (out.dtype if out is not None else q.dtype)
     if out is None:
         out = torch.empty((B, h, d), dtype=out_dtype, device=dev)
     elif out.shape != q.shape or out.dtype != out_dtype:
@@ -184,7 +187,7 @@ def gqe_routed_prefill(q, k, v, router_logits, top_k: int, causal: bool = True,
         raise ValueError("router_logits must be float32 [B,T,h]")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share one dtype")
-    out_dtype = out_dtype or q.dtype
+    out_dtype = out_dtype or (out.dtype if out is not None else q.dtype)
     if out is None:
         out = torch.empty((B, h, T, d), dtype=out_dtype, device=dev)
     elif out.shape != q.shape or out.dtype != out_dtype:
@@ -200,4 +203,43 @@ def gqe_routed_prefill(q, k, v, router_logits, top_k: int, causal: bool = True,
                                  _dt(q, "q"), _dt(out, "out"), scale, int(bool(causal)),
                                  _stream(dev))
     _check("gqe_routed_prefill", st)
+    return out, idx, gate
+
+
+def gqe_routed_decode(q, k_cache, v_cache, lens, router_logits, top_k: int,
+                      scale: float | None = None, out=None, out_dtype=None, workspace=None):
+    """GQE routed decode. q [B,h,d], caches [B,g,T_max,d], lens [B] int32,
+    router_logits [B,h] float32 -> (out [B,h,d], idx [B,g,k] int32, gate [B,g,k] fp32)."""
+    dev = _dev(q, k_cache, v_cache, lens, router_logits)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,h,d] and caches [B,g,T_max,d]")
+    B, h, d = q.shape
+    if k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError("cache shape does not match q")
+    if lens.dtype != torch.int32 or lens.shape != (B,):
+        raise ValueError("lens must be int32 [B]")
+    if router_logits.dtype != torch.float32 or router_logits.shape != (B, h):
+        raise ValueError("router_logits must be float32 [B,h]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    g, T_max = k_cache.shape[1], k_cache.shape[2]
+    out_dtype = out_dtype or (out.dtype if out is not None else q.dtype)
+    if out is None:
+        out = torch.empty((B, h, d), dtype=out_dtype, device=dev)
+    elif out.shape != q.shape or out.dtype != out_dtype:
+        raise ValueError("out must be [B,h,d] of out_dtype")
+    _dev(q, out)
+    kk = max(int(top_k), 1)
+    idx = torch.empty((B, g, kk), dtype=torch.int32, device=dev)
+    gate = torch.empty((B, g, kk), dtype=torch.float32, device=dev)
+    need = gqa_decode_workspace_bytes(B, h, g, T_max, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = _lib.gqe_routed_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                lens.data_ptr(), router_logits.data_ptr(), int(top_k),
+                                out.data_ptr(), idx.data_ptr(), gate.data_ptr(), B, h, g, T_max, d,
+                                _dt(q, "q"), _dt(out, "out"), scale, workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream(dev))
+    _check("gqe_routed_decode", st)
     return out, idx, gate

@@ -81,6 +81,46 @@ DecodeLayout decode_layout(int h, int g, int d) {
   return L;
 }
 
+// Argument checks shared by the two decode entry points (no HIP call); on
+// success fills p (everything but the routing fields). B == 0 is accepted
+// before pointers are looked at.
+gqa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* lens,
+                          void* out, int B, int h, int g, int T_max, int d, gqa_dtype in_dtype,
+                          gqa_dtype out_dtype, float scale, void* workspace, size_t workspace_bytes,
+                          gqa::DecodeParams& p) {
+  if (B < 0 || T_max < 0) return fail(GQA_ERR_INVALID_ARG, "B=%d and T_max=%d must be >= 0", B, T_max);
+  if (h < 1 || g < 1) return fail(GQA_ERR_INVALID_ARG, "h=%d and g=%d must be >= 1", h, g);
+  if (h % g != 0) return fail(GQA_ERR_INVALID_ARG, "g=%d must divide h=%d", g, h);
+  if (d < 1) return fail(GQA_ERR_INVALID_ARG, "d=%d must be >= 1", d);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(GQA_ERR_INVALID_ARG, "unknown dtype (in %d, out %d)", in_dtype, out_dtype);
+  if (!(std::isfinite(scale) && scale > 0.0f))
+    return fail(GQA_ERR_INVALID_ARG, "scale=%g must be finite and > 0", (double)scale);
+  if ((long long)g * T_max >= (1ll << 31))
+    return fail(GQA_ERR_INVALID_ARG, "g*T_max=%lld exceeds the 2^31 row limit", (long long)g * T_max);
+  if (B == 0) return GQA_OK;
+  if (!q || !out || !lens) return fail(GQA_ERR_INVALID_ARG, "null q, out or lens pointer");
+  if (T_max > 0 && (!k_cache || !v_cache)) return fail(GQA_ERR_INVALID_ARG, "null cache pointer");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(GQA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (in_dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "decode supports bf16 caches only");
+  if (!gqa::decode_supports(d)) return fail(GQA_ERR_UNSUPPORTED, "decode supports d in {64, 128}, got %d", d);
+  if (h / g > 64) return fail(GQA_ERR_UNSUPPORTED, "decode supports h/g <= 64, got %d", h / g);
+  const DecodeLayout L = decode_layout(h, g, d);
+  if (workspace_bytes < L.total)
+    return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, L.total);
+  if (!workspace || !aligned16(workspace))
+    return fail(GQA_ERR_INVALID_ARG, "workspace must be a 16-byte aligned device pointer");
+  p.q = q; p.k_cache = k_cache; p.v_cache = v_cache; p.lens = lens; p.out = out;
+  p.B = B; p.h = h; p.g = g; p.T_max = T_max; p.d = d;
+  p.n_units = L.n_units;
+  p.part_acc = static_cast<float*>(workspace);
+  p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.acc_bytes);
+  p.scale = scale;
+  p.out_bf16 = out_dtype == GQA_BF16;
+  return GQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -136,40 +176,37 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache, c
                       gqa_dtype out_dtype, float scale, void* workspace, size_t workspace_bytes,
                       void* stream) {
   g_last_error[0] = '\0';
-  if (B < 0 || T_max < 0) return fail(GQA_ERR_INVALID_ARG, "B=%d and T_max=%d must be >= 0", B, T_max);
-  if (h < 1 || g < 1) return fail(GQA_ERR_INVALID_ARG, "h=%d and g=%d must be >= 1", h, g);
-  if (h % g != 0) return fail(GQA_ERR_INVALID_ARG, "g=%d must divide h=%d", g, h);
-  if (d < 1) return fail(GQA_ERR_INVALID_ARG, "d=%d must be >= 1", d);
-  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
-    return fail(GQA_ERR_INVALID_ARG, "unknown dtype (in %d, out %d)", in_dtype, out_dtype);
-  if (!(std::isfinite(scale) && scale > 0.0f))
-    return fail(GQA_ERR_INVALID_ARG, "scale=%g must be finite and > 0", (double)scale);
-  if ((long long)g * T_max >= (1ll << 31))
-    return fail(GQA_ERR_INVALID_ARG, "g*T_max=%lld exceeds the 2^31 row limit", (long long)g * T_max);
-  if (B == 0) return GQA_OK;
-  if (!q || !out || !lens) return fail(GQA_ERR_INVALID_ARG, "null q, out or lens pointer");
-  if (T_max > 0 && (!k_cache || !v_cache)) return fail(GQA_ERR_INVALID_ARG, "null cache pointer");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
-    return fail(GQA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-  if (in_dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "decode supports bf16 caches only");
-  if (!gqa::decode_supports(d)) return fail(GQA_ERR_UNSUPPORTED, "decode supports d in {64, 128}, got %d", d);
-  if (h / g > 64) return fail(GQA_ERR_UNSUPPORTED, "decode supports h/g <= 64, got %d", h / g);
-  const DecodeLayout L = decode_layout(h, g, d);
-  if (workspace_bytes < L.total)
-    return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, L.total);
-  if (L.total && (!workspace || !aligned16(workspace)))
-    return fail(GQA_ERR_INVALID_ARG, "workspace must be a 16-byte aligned device pointer");
-  gqa_status s = check_device();
-  if (s != GQA_OK) return s;
   gqa::DecodeParams p{};
-  p.q = q; p.k_cache = k_cache; p.v_cache = v_cache; p.lens = lens; p.out = out;
-  p.B = B; p.h = h; p.g = g; p.T_max = T_max; p.d = d;
-  p.n_units = L.n_units;
-  p.part_acc = static_cast<float*>(workspace);
-  p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.acc_bytes);
-  p.scale = scale;
-  p.out_bf16 = out_dtype == GQA_BF16;
+  gqa_status s = prepare_decode(q, k_cache, v_cache, lens, out, B, h, g, T_max, d, in_dtype, out_dtype,
+                                scale, workspace, workspace_bytes, p);
+  if (s != GQA_OK || B == 0) return s;
+  if ((s = check_device()) != GQA_OK) return s;
   return hip_status(gqa::launch_decode(p, static_cast<hipStream_t>(stream)), "gqa_decode launch");
+}
+
+gqa_status gqe_routed_decode(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* lens, const float* router_logits, int top_k, void* out,
+                             int32_t* topk_idx, float* topk_gate, int B, int h, int g, int T_max,
+                             int d, gqa_dtype in_dtype, gqa_dtype out_dtype, float scale,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  gqa::DecodeParams p{};
+  gqa_status s = prepare_decode(q, k_cache, v_cache, lens, out, B, h, g, T_max, d, in_dtype, out_dtype,
+                                scale, workspace, workspace_bytes, p);
+  if (s != GQA_OK) return s;
+  const int r = h / g;
+  if (top_k < 1 || top_k > r) return fail(GQA_ERR_INVALID_ARG, "top_k=%d must be in [1, h/g=%d]", top_k, r);
+  if (B == 0) return GQA_OK;
+  if (!router_logits || !topk_idx || !topk_gate)
+    return fail(GQA_ERR_INVALID_ARG, "null router_logits, topk_idx or topk_gate pointer");
+  if ((s = check_device()) != GQA_OK) return s;
+  auto st = static_cast<hipStream_t>(stream);
+  gqa::RouterParams rp{router_logits, topk_idx, topk_gate, B, 1, h, g, top_k};
+  if ((s = hip_status(gqa::launch_router(rp, st), "gqe decode router launch")) != GQA_OK) return s;
+  p.idx = topk_idx;
+  p.gate = topk_gate;
+  p.top_k = top_k;
+  return hip_status(gqa::launch_decode(p, st), "gqe routed decode launch");
 }
 
 gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v, const float* router_logits,

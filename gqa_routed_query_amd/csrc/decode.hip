@@ -70,9 +70,12 @@ struct KArgs {
   const uint16_t* vc;
   const int32_t* lens;
   void* out;
-  float* part_acc;  // [n_units, 2, r, D]
-  float* part_ml;   // [n_units, 2, r, 2]: reference max (log2 units), sum
+  float* part_acc;  // [n_units, 2, R, D]
+  float* part_ml;   // [n_units, 2, R, 2]: reference max (log2 units), sum
+  const int32_t* idx;  // routed: [B, g, R] global head ids of the kept heads, else null
+  const float* gate;   // routed: [B, g, R] gates, else null
   int B, h, g, r, T_max;
+  int R;            // rows per KV group: r (dense) or the kept heads k (routed)
   int n_units;      // workgroups sharing the key range
   float c;          // scale * log2(e)
   int out_bf16;
@@ -83,6 +86,12 @@ __device__ __forceinline__ int seq_len(const KArgs& a, int b) {
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Global query head of row e (< R) of KV group gam of sequence b.
+template <bool ROUTED>
+__device__ __forceinline__ int head_of(const KArgs& a, int b, int gam, int e) {
+  return ROUTED ? a.idx[((size_t)b * a.g + gam) * a.R + e] : gam * a.r + e;
+}
 
 // Keys of all streams: g * sum_b lens[b]. Every lane returns the total.
 __device__ __forceinline__ long long total_keys(const KArgs& a, int lane) {
@@ -158,18 +167,18 @@ __device__ __forceinline__ bool next_piece(const KArgs& a, const Piece& p, long 
   return true;
 }
 
-template <int D, int HB>
+template <int D, int HB, bool ROUTED>
 __device__ __forceinline__ void load_q(const KArgs& a, const Piece& p, int grp, int i16,
                                        bf16x8 (&qf)[HB][DTile<D>::kDS]) {
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int e = hb * 16 + i16;
-    const uint16_t* qrow =
-        a.q + ((size_t)p.b * a.h + p.gam * a.r + min(e, a.r - 1)) * D + grp * (D / 4);
+    const int head = head_of<ROUTED>(a, p.b, p.gam, min(e, a.R - 1));
+    const uint16_t* qrow = a.q + ((size_t)p.b * a.h + head) * D + grp * (D / 4);
 #pragma unroll
     for (int ds = 0; ds < DTile<D>::kDS; ++ds) {
       bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 8 * ds);
-      if (e >= a.r) x = bf16x8{};
+      if (e >= a.R) x = bf16x8{};
       qf[hb][ds] = x;
     }
   }
@@ -216,7 +225,7 @@ __device__ __forceinline__ bool next_sub(const KArgs& a, Piece& p, long long& po
   }
 }
 
-template <int D, int HB>
+template <int D, int HB, bool ROUTED>
 __global__ __launch_bounds__(kThreads) void decode_kernel(KArgs a) {
   using L = DTile<D>;
   constexpr int kCP = D + 4;                     // combine row: D values, max, sum, 16-byte pitch
@@ -258,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KArgs a) {
   float* comb = reinterpret_cast<float*>(smem);
 
   for (int pi = 0;; ++pi) {
-    load_q<D, HB>(a, cur, grp, i16, qf);
+    load_q<D, HB, ROUTED>(a, cur, grp, i16, qf);
     f32x4 o[HB][D / 16];
     float m_run[HB], l_run[HB];
 #pragma unroll
@@ -371,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KArgs a) {
         const int hh = x / D;
         const int d = x - hh * D;
         const int e = hb * 16 + hh;
-        if (e >= a.r) break;  // x only grows
+        if (e >= a.R) break;  // x only grows
         float M = -INFINITY;
 #pragma unroll
         for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, comb[(wv * 16 + hh) * kCP + D]);
@@ -385,14 +394,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KArgs a) {
           den += sc * src[D + 1];
         }
         if (whole) {
-          const size_t off = ((size_t)cur.b * a.h + cur.gam * a.r + e) * D + d;
-          const float y = acc / den;
+          const int head = head_of<ROUTED>(a, cur.b, cur.gam, e);
+          const size_t off = ((size_t)cur.b * a.h + head) * D + d;
+          float y = acc / den;
+          if (ROUTED) y *= a.gate[((size_t)cur.b * a.g + cur.gam) * a.R + e];
           if (a.out_bf16)
             static_cast<uint16_t*>(a.out)[off] = static_cast<uint16_t>(pack_bf16x2(y, 0.0f) & 0xffffu);
           else
             static_cast<float*>(a.out)[off] = y;
         } else {
-          const size_t prow = ((size_t)unit * 2 + slot) * a.r + e;
+          const size_t prow = ((size_t)unit * 2 + slot) * a.R + e;
           a.part_acc[prow * D + d] = acc;
           if (d == 0) {
             a.part_ml[prow * 2 + 0] = M;
@@ -410,8 +421,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KArgs a) {
 
 // One wave per (sequence, head): a stream cut over several shares has its
 // pieces merged by log-sum-exp; a sequence with no cached keys gets a zero
-// row. Streams that lie in one share were written by decode_kernel.
-template <int D>
+// row, and so does (routed) a head the router did not keep. Streams that lie
+// in one share were written by decode_kernel.
+template <int D, bool ROUTED>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);  // b * h + head
@@ -419,8 +431,25 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
   const int b = row / a.h;
   const int head = row - b * a.h;
   const int gam = head / a.r;
-  const int e = head - gam * a.r;
+  int e = head - gam * a.r;  // the head's row in its group
   constexpr int EPL = D / 64;
+  if (ROUTED) {
+    const int32_t* sel = a.idx + ((size_t)b * a.g + gam) * a.R;
+    e = -1;
+    for (int j = 0; j < a.R; ++j)
+      if (sel[j] == head) e = j;
+    if (e < 0) {
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) {
+        const size_t off = (size_t)row * D + lane + 64 * x;
+        if (a.out_bf16)
+          static_cast<uint16_t*>(a.out)[off] = 0;
+        else
+          static_cast<float*>(a.out)[off] = 0.0f;
+      }
+      return;
+    }
+  }
   // Global position of the stream, g * (keys of sequences before b) + gam *
   // len, and the total, from one pass over lens.
   long long before = 0, total = 0;
@@ -457,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
   const int slot0 = (long long)u0 * share < start ? 1 : 0;
   const int n = u1 - u0 + 1;
   auto prow_of = [&](int j) {
-    return ((size_t)(u0 + j) * 2 + (j == 0 ? slot0 : 0)) * a.r + e;
+    return ((size_t)(u0 + j) * 2 + (j == 0 ? slot0 : 0)) * a.R + e;
   };
   // Pieces in rounds of 64: lane j holds piece j's (max, sum); the
   // accumulator loads do not depend on the max, so a round issues together.
@@ -492,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
     }
     M = Mn;
   }
-  const float inv = 1.0f / den;
+  const float inv = (ROUTED ? a.gate[((size_t)b * a.g + gam) * a.R + e] : 1.0f) / den;
 #pragma unroll
   for (int x = 0; x < EPL; ++x) {
     const float y = acc[x] * inv;
@@ -504,16 +533,11 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
   }
 }
 
-template <int D, int HB>
-const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&decode_kernel<D, HB>);
-}
-
 template <int D>
 const void* kernel_for_hb(int hb) {
-  if (hb == 1) return kernel_ptr<D, 1>();
-  if (hb == 2) return kernel_ptr<D, 2>();
-  if (hb <= 4) return kernel_ptr<D, 4>();
+  if (hb == 1) return reinterpret_cast<const void*>(&decode_kernel<D, 1, false>);
+  if (hb == 2) return reinterpret_cast<const void*>(&decode_kernel<D, 2, false>);
+  if (hb <= 4) return reinterpret_cast<const void*>(&decode_kernel<D, 4, false>);
   return nullptr;
 }
 
@@ -521,6 +545,25 @@ const void* decode_kernel_for(int d, int hb) {
   if (d == 64) return kernel_for_hb<64>(hb);
   if (d == 128) return kernel_for_hb<128>(hb);
   return nullptr;
+}
+
+template <int D, bool ROUTED>
+hipError_t launch_dr(const KArgs& a, const dim3 grid, hipStream_t stream) {
+  const dim3 block(kThreads);
+  const int hb = div_up(a.R, 16);
+  if (hb == 1)
+    hipLaunchKernelGGL((decode_kernel<D, 1, ROUTED>), grid, block, 0, stream, a);
+  else if (hb == 2)
+    hipLaunchKernelGGL((decode_kernel<D, 2, ROUTED>), grid, block, 0, stream, a);
+  else if (hb <= 4)
+    hipLaunchKernelGGL((decode_kernel<D, 4, ROUTED>), grid, block, 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D, ROUTED>), dim3(div_up(a.B * a.h, kWaves)), block, 0,
+                     stream, a);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -533,28 +576,19 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   a.out = p.out;
   a.part_acc = p.part_acc;
   a.part_ml = p.part_ml;
+  a.idx = p.idx;
+  a.gate = p.gate;
   a.B = p.B;
   a.h = p.h;
   a.g = p.g;
   a.r = p.h / p.g;
+  a.R = p.idx ? p.top_k : a.r;
   a.T_max = p.T_max;
   a.n_units = p.n_units;
   a.c = p.scale * kLog2e;
   a.out_bf16 = p.out_bf16;
-  const dim3 grid(p.n_units), block(kThreads);
-  const int hb = div_up(a.r, 16);
-  if (hb == 1)
-    hipLaunchKernelGGL((decode_kernel<D, 1>), grid, block, 0, stream, a);
-  else if (hb == 2)
-    hipLaunchKernelGGL((decode_kernel<D, 2>), grid, block, 0, stream, a);
-  else if (hb <= 4)
-    hipLaunchKernelGGL((decode_kernel<D, 4>), grid, block, 0, stream, a);
-  else
-    return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(div_up(p.B * p.h, kWaves)), block, 0, stream, a);
-  return hipGetLastError();
+  const dim3 grid(p.n_units);
+  return p.idx ? launch_dr<D, true>(a, grid, stream) : launch_dr<D, false>(a, grid, stream);
 }
 
 }  // namespace

@@ -44,6 +44,9 @@ struct DecodeParams {
   void* out;            // [B, h, d]
   float* part_acc;      // [n_units, 2, h/g, d] fp32 workspace
   float* part_ml;       // [n_units, 2, h/g, 2] fp32 workspace
+  const int32_t* idx;   // routed: [B, g, top_k] kept heads (router output), else null
+  const float* gate;    // routed: [B, g, top_k] their gates, else null
+  int top_k;            // routed: kept heads per group
   int B, h, g, T_max, d;
   int n_units;          // waves that share the key range
   float scale;

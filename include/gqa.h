@@ -115,6 +115,33 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * GQE routed decode: one new token per sequence over a KV cache, with the
+ * router of gqe_routed_prefill applied to that token (gist.science explainer
+ * of "Grouped Query Experts", section "Architecture et Routage": top-k query
+ * head experts per KV group, the key/value path stays dense).
+ *   q, k_cache, v_cache, lens, out, workspace: as for gqa_decode (the same
+ *           gqa_decode_workspace_bytes(...) bytes suffice).
+ *   router_logits [B, h] fp32, device: the router's score of every head for
+ *           the new token.
+ *   top_k   experts kept per group, 1 <= top_k <= h/g <= 64.
+ *   topk_idx  [B, g, top_k] int32, written: kept heads in rank order (higher
+ *           logit first, equal logits by lower head id).
+ *   topk_gate [B, g, top_k] fp32, written: softmax of the kept logits.
+ *   out [B, h, d] out_dtype, written in full: a kept head's row is gate times
+ *           the plain decode row of that head (every cached key of its group
+ *           below lens[b]); every other row is 0, as is every row of a
+ *           sequence with lens[b] = 0.
+ * Supported and errors: as for gqa_decode, plus GQA_ERR_INVALID_ARG for
+ * top_k outside [1, h/g] or a null router pointer.
+ */
+gqa_status gqe_routed_decode(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* lens, const float* router_logits, int top_k,
+                             void* out, int32_t* topk_idx, float* topk_gate,
+                             int B, int h, int g, int T_max, int d,
+                             gqa_dtype in_dtype, gqa_dtype out_dtype, float scale,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * GQE routed prefill.
  *   q [B, h, T, d], k/v [B, g, T, d] in_dtype, as for gqa_prefill.
  *   router_logits [B, T, h] fp32, device: the router's score of every query

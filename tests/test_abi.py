@@ -119,11 +119,38 @@ def test_gqe_rejects(kw, status):
     assert _gqe(**kw) == status
 
 
+def _gqe_decode(**kw):
+    a = dict(q=P, kc=P, vc=P, lens=P, lg=P, k_top=1, out=P, idx=P, gate=P, B=2, h=8, g=2, T=1024,
+             d=128, i=BF16, o=BF16, scale=0.088, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.gqe_routed_decode(a["q"], a["kc"], a["vc"], a["lens"], a["lg"], a["k_top"], a["out"],
+                                 a["idx"], a["gate"], a["B"], a["h"], a["g"], a["T"], a["d"], a["i"],
+                                 a["o"], a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_top=0), INVALID),
+    (dict(k_top=5), INVALID),              # more than h/g = 4
+    (dict(lg=None), INVALID),
+    (dict(gate=None), INVALID),
+    (dict(h=8, g=3), INVALID),
+    (dict(i=F32), UNSUPPORTED),
+    (dict(wsb=0), WORKSPACE),
+])
+def test_gqe_decode_rejects(kw, status):
+    assert _gqe_decode(**kw) == status
+
+
+def test_gqe_decode_empty_batch_is_ok():
+    assert _gqe_decode(B=0, q=None, lg=None) == OK
+
+
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible: would launch")
 def test_valid_calls_report_no_device():
     assert _prefill() == NO_DEVICE
     assert _decode() == NO_DEVICE
     assert _gqe() == NO_DEVICE
+    assert _gqe_decode() == NO_DEVICE
 
 
 def test_kv_cache_bytes_matches_oracle_law():
