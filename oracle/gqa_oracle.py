@@ -53,6 +53,7 @@ __all__ = [
     "gqe_topk_ref",
     "gqe_ref",
     "gqe_decode_ref",
+    "gqe_router_ref",
     "kv_cache_bytes",
     "gqe_active_query_heads",
 ]
@@ -267,6 +268,34 @@ def gqe_decode_ref(q, k_cache, v_cache, lens, logits, top_k: int,
                 i = int(idx[b, gam, j])
                 out[b, i] = gate[b, gam, j] * dense[b, i]
     return out, idx, gate
+
+
+def gqe_router_ref(x, w_r, g: int, top_k: int):
+    """GQE router: score every query-head expert for every token, then keep
+    top_k per KV group -> (logits [N,h] float64, bound [N,h], idx, gate).
+
+    x [N, d_model] holds the tokens' input vectors and w_r [h, d_model] one
+    row of router weights per query head; logits = x @ w_r^T. The pages say
+    the router examines each token and picks the experts of each group
+    (gist.science GQE explainer, sections "Architecture et Routage" and the
+    router analogy before it) without fixing its form; a linear map of the
+    token, as for the Q/K/V projections of the attention layer (IBM Think
+    page, the weight matrices W_Q, W_K, W_V), is the reading taken here.
+
+    bound is the classical worst-case error of a float32 dot product of
+    length n in any summation order: n * 2^-24 * sum_i |x_i w_i| (a GPU that
+    accumulates in fp32 stays within it). idx and gate are gqe_topk_ref of
+    the logits, laid out [N, g, k].
+    """
+    xf, wf = _f64(x), _f64(w_r)
+    if xf.ndim != 2 or wf.ndim != 2 or xf.shape[1] != wf.shape[1]:
+        raise ValueError("need x [N, d_model] and w_r [h, d_model]")
+    n_tok, dm = xf.shape
+    h = wf.shape[0]
+    logits = xf @ wf.T
+    bound = dm * 2.0 ** -24 * (np.abs(xf) @ np.abs(wf).T)
+    idx, gate = gqe_topk_ref(logits.reshape(1, n_tok, h), g, top_k)
+    return logits, bound, idx[0], gate[0]
 
 
 def kv_cache_bytes(B: int, n_kv: int, T: int, d: int, elt_bytes: int,

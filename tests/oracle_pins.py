@@ -379,6 +379,24 @@ def pin_gqe_decode():
     assert np.all(out0[0] == 0) and np.all(out0[2] == 0) and np.abs(out0[1]).sum() > 0
 
 
+def pin_gqe_router():
+    """Router logits equal torch's linear layer (x W^T, float64); the kept
+    experts and gates equal gqe_topk_ref of those logits; the fp32 error bound
+    covers a float32 evaluation of the same dot products (torch, float32)."""
+    n, dm, h, g = 37, 96, 16, 4
+    x = _rand((n, dm), 200)
+    w = _rand((h, dm), 201) / math.sqrt(dm)
+    logits, bound, idx, gate = orc.gqe_router_ref(x, w, g, 2)
+    ref = torch.nn.functional.linear(torch.from_numpy(x), torch.from_numpy(w)).numpy()
+    assert np.abs(logits - ref).max() < 1e-12
+    ridx, rgate = orc.gqe_topk_ref(ref.reshape(1, n, h), g, 2)
+    assert np.array_equal(idx, ridx[0]) and np.abs(gate - rgate[0]).max() < 1e-15
+    f32 = torch.nn.functional.linear(torch.from_numpy(x).float(), torch.from_numpy(w).float())
+    err = np.abs(f32.double().numpy() - ref)
+    assert np.all(err <= bound) and bound.max() < 1e-3
+    assert idx.shape == (n, g, 2) and gate.shape == (n, g, 2)
+
+
 # --------------------------------------------------------------------------
 # Accounting printed on the pages
 # --------------------------------------------------------------------------
@@ -424,6 +442,7 @@ PINS = [
     pin_gates,
     pin_gqe_structure,
     pin_gqe_decode,
+    pin_gqe_router,
     pin_kv_cache_law,
     pin_gqe_active_count,
 ]

@@ -110,6 +110,10 @@ def _gqe_decode_no_zero(q, kc, vc, lens, logits, top_k, scale=None):
     return np.where(np.abs(out).sum(-1, keepdims=True) > 0, out, dense), idx, gate
 
 
+def _router_dropped_feature(x, w_r, g, top_k):   # the last input feature ignored
+    return _orig["gqe_router_ref"](np.asarray(x)[:, :-1], np.asarray(w_r)[:, :-1], g, top_k)
+
+
 def _active_no_shared(g, top_k, shared=1):
     return g * top_k
 
@@ -131,6 +135,7 @@ MUTATIONS = {
     "gqe/gate_dropped": ("gqe_ref", _gqe_no_gate),
     "gqe_decode/gate_dropped": ("gqe_decode_ref", _gqe_decode_no_gate),
     "gqe_decode/unselected_not_zero": ("gqe_decode_ref", _gqe_decode_no_zero),
+    "gqe_router/dropped_feature": ("gqe_router_ref", _router_dropped_feature),
     "kv_cache_bytes/no_factor_two": ("kv_cache_bytes", _kv_bytes_no_two),
     "kv_head_of/strided": ("kv_head_of", _kv_head_strided),
     "active_heads/no_shared": ("gqe_active_query_heads", _active_no_shared),
