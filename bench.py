@@ -111,8 +111,8 @@ def main():
     import torch
 
     import gqa_routed_query_amd as gq
-    from workloads import (WORKLOADS, decode_inputs, gqe_inputs, gqe_sweep_points, prefill_inputs,
-                           router_logits)
+    from workloads import (ROUTER_D_MODEL, WORKLOADS, decode_inputs, gqe_inputs, gqe_sweep_points,
+                           prefill_inputs, router_inputs, router_logits)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -273,6 +273,30 @@ def main():
             del q, kc, vc, out, wsb
             torch.cuda.empty_cache()
 
+    # ---- GQE router with its projection (x W_r^T + top-k), outside the step ----
+    grouter = {}
+    if run_gqe and not args.no_sweep:
+        n_tok = wg.B * wg.T
+        rx, rw = router_inputs(n_tok, ROUTER_D_MODEL, wg.h, seed=wg.seed + 200, device=dev)
+        for kk in wg.top_k:
+            tm = Timer(torch)
+            for it in range(3 + args.steps):
+                flush.sum()
+                if it < 3:
+                    gq.gqe_router(rx, rw, wg.g, kk)
+                    continue
+                with tm:
+                    gq.gqe_router(rx, rw, wg.g, kk)
+            torch.cuda.synchronize()
+            sr = stats(tm.ms())
+            # x and w_r read once; logits, idx and gates written
+            nb = rx.numel() * 2 + rw.numel() * 2 + n_tok * wg.h * 4 + 2 * n_tok * wg.g * kk * 4
+            grouter[f"top{kk}"] = dict(mean_us=sr["mean_ms"] * 1e3, bytes_per_call=nb,
+                                       GBps=nb / (sr["mean_ms"] * 1e-3) / 1e9,
+                                       frac=nb / (sr["mean_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS)
+            log(f"gqe router k={kk}: {sr['mean_ms']*1e3:.1f} us/call, {grouter[f'top{kk}']['GBps']:.0f} GB/s")
+        del rx, rw
+
     # ---- GQE vs dense GQA over the sequence length, outside the step ----
     gsweep = []
     if run_gqe and not args.no_sweep:
@@ -367,6 +391,8 @@ def main():
         line["gqe_sweep"] = gsweep
     if gdec:
         line["gqe_decode"] = gdec
+    if grouter:
+        line["gqe_router"] = dict(grouter, n_tokens=wg.B * wg.T, d_model=ROUTER_D_MODEL, h=wg.h, g=wg.g)
     if cpu:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -9,10 +9,11 @@ this package only marshals torch tensors into its entry points:
 * :func:`gqe_routed_prefill` -- GQE: top-k query-head experts per KV group
   per token, dense K/V.
 * :func:`gqe_routed_decode` -- GQE routing applied to one decode step.
+* :func:`gqe_router` -- the router's projection x W_r^T fused with the top-k.
 
 torch provides device memory and the stream; every step of the computation
 runs in the library's kernels. Importing the package fails loudly when the
-library has not been built (``python -m gqa_routed_query_amd.build``).
+library has not been built (``python gqa_routed_query_amd/build.py``).
 """
 from ._binding import (  # noqa: F401
     GQA_BF16,
@@ -25,6 +26,7 @@ from ._binding import (  # noqa: F401
     gqa_prefill,
     gqe_routed_decode,
     gqe_routed_prefill,
+    gqe_router,
     last_error,
     lib_path,
     status_string,

@@ -34,7 +34,7 @@ class GqaError(RuntimeError):
 def _load():
     if not os.path.exists(lib_path):
         raise ImportError(
-            f"{lib_path} is not built; run `python -m gqa_routed_query_amd.build` "
+            f"{lib_path} is not built; run `python gqa_routed_query_amd/build.py` "
             "(hipcc, gfx950)")
     lib = ctypes.CDLL(lib_path)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -53,6 +53,8 @@ def _load():
     lib.gqe_routed_decode.restype = i32
     lib.gqe_routed_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32,
                                       i32, i32, i32, f32, vp, sz, vp]
+    lib.gqe_router.restype = i32
+    lib.gqe_router.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.gqa_kv_cache_bytes.restype = ctypes.c_uint64
     lib.gqa_kv_cache_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.gqa_status_string.restype = ctypes.c_char_p
@@ -243,3 +245,30 @@ def gqe_routed_decode(q, k_cache, v_cache, lens, router_logits, top_k: int,
                                 workspace.numel() * workspace.element_size(), _stream(dev))
     _check("gqe_routed_decode", st)
     return out, idx, gate
+
+
+def gqe_router(x, w_r, g: int, top_k: int, return_logits: bool = True):
+    """GQE router with its projection. x [..., d_model] bf16 (tokens),
+    w_r [h, d_model] bf16 -> (logits [..., h] fp32 or None, idx [..., g, k] int32,
+    gate [..., g, k] fp32)."""
+    dev = _dev(x, w_r)
+    if w_r.dim() != 2 or x.shape[-1] != w_r.shape[1]:
+        raise ValueError("expected x [..., d_model] and w_r [h, d_model]")
+    if x.dtype != w_r.dtype:
+        raise TypeError("x and w_r must share one dtype")
+    if not x.is_contiguous() or not w_r.is_contiguous():
+        raise ValueError("x and w_r must be contiguous")
+    lead = tuple(x.shape[:-1])
+    n_tok = 1
+    for s_ in lead:
+        n_tok *= s_
+    h, d_model = w_r.shape
+    kk = max(int(top_k), 1)
+    idx = torch.empty(lead + (g, kk), dtype=torch.int32, device=dev)
+    gate = torch.empty(lead + (g, kk), dtype=torch.float32, device=dev)
+    logits = torch.empty(lead + (h,), dtype=torch.float32, device=dev) if return_logits else None
+    st = _lib.gqe_router(x.data_ptr(), w_r.data_ptr(), int(top_k),
+                         logits.data_ptr() if logits is not None else None, idx.data_ptr(),
+                         gate.data_ptr(), n_tok, d_model, h, int(g), _dt(x, "x"), _stream(dev))
+    _check("gqe_router", st)
+    return logits, idx, gate

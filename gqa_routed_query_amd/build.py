@@ -1,6 +1,8 @@
 """Build libgqa.so (HIP, gfx950) in place, next to this file.
 
-Usage: ``python -m gqa_routed_query_amd.build`` or ``build()`` from Python.
+Usage: ``python gqa_routed_query_amd/build.py`` (run as a script: the package
+itself cannot be imported before the library exists), or ``build()`` from
+``__graft_entry__``. Only the standard library is imported here.
 The library is compiled with hipcc for gfx950 only. Packed fp32 instructions
 are disabled for all device code (``-packed-fp32-ops``); the host pass warns
 that it does not know that target feature, which is harmless.

@@ -209,6 +209,29 @@ gqa_status gqe_routed_decode(const void* q, const void* k_cache, const void* v_c
   return hip_status(gqa::launch_decode(p, st), "gqe routed decode launch");
 }
 
+gqa_status gqe_router(const void* x, const void* w_r, int top_k, float* logits, int32_t* topk_idx,
+                      float* topk_gate, int n_tokens, int d_model, int h, int g, gqa_dtype in_dtype,
+                      void* stream) {
+  g_last_error[0] = '\0';
+  if (n_tokens < 0 || d_model < 1) return fail(GQA_ERR_INVALID_ARG, "n_tokens=%d must be >= 0 and d_model=%d >= 1", n_tokens, d_model);
+  if (h < 1 || g < 1) return fail(GQA_ERR_INVALID_ARG, "h=%d and g=%d must be >= 1", h, g);
+  if (h % g != 0) return fail(GQA_ERR_INVALID_ARG, "g=%d must divide h=%d", g, h);
+  const int r = h / g;
+  if (top_k < 1 || top_k > r) return fail(GQA_ERR_INVALID_ARG, "top_k=%d must be in [1, h/g=%d]", top_k, r);
+  if (!valid_dtype(in_dtype)) return fail(GQA_ERR_INVALID_ARG, "unknown dtype %d", in_dtype);
+  if (in_dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "the router projection takes bf16 x and w_r");
+  if (!gqa::router_proj_supports(d_model, h))
+    return fail(GQA_ERR_UNSUPPORTED, "router projection supports h <= 64 and d_model a multiple of 128, got h=%d d_model=%d", h, d_model);
+  if (n_tokens == 0) return GQA_OK;
+  if (!x || !w_r || !topk_idx || !topk_gate)
+    return fail(GQA_ERR_INVALID_ARG, "null x, w_r, topk_idx or topk_gate pointer");
+  if (!aligned16(x) || !aligned16(w_r)) return fail(GQA_ERR_INVALID_ARG, "x and w_r must be 16-byte aligned");
+  gqa_status s = check_device();
+  if (s != GQA_OK) return s;
+  gqa::RouterProjParams p{x, w_r, logits, topk_idx, topk_gate, n_tokens, d_model, h, g, top_k};
+  return hip_status(gqa::launch_router_proj(p, static_cast<hipStream_t>(stream)), "gqe_router launch");
+}
+
 gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v, const float* router_logits,
                               int top_k, void* out, int32_t* topk_idx, float* topk_gate, int B, int h,
                               int g, int T, int d, gqa_dtype in_dtype, gqa_dtype out_dtype, float scale,

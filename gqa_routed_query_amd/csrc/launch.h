@@ -36,6 +36,15 @@ struct RouterParams {
   int B, T, h, g, k;
 };
 
+struct RouterProjParams {
+  const void* x;        // [n_tok, d_model] bf16
+  const void* w;        // [h, d_model] bf16
+  float* logits;        // [n_tok, h] or null
+  int32_t* idx;         // [n_tok, g, k]
+  float* gate;          // [n_tok, g, k]
+  int n_tok, d_model, h, g, k;
+};
+
 struct DecodeParams {
   const void* q;        // [B, h, d] bf16
   const void* k_cache;  // [B, g, T_max, d] bf16
@@ -56,12 +65,14 @@ struct DecodeParams {
 hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
 hipError_t launch_router(const RouterParams& p, hipStream_t stream);
+hipError_t launch_router_proj(const RouterProjParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
 // Head dims with a bf16 MFMA prefill kernel / an fp32 kernel / a decode kernel.
 bool attn_bf16_supports(int d);
 bool attn_f32_supports(int d);
 bool decode_supports(int d);
+bool router_proj_supports(int d_model, int h);
 
 // Waves that share a decode call's key range (honours GQA_DECODE_UNITS).
 int decode_units(int h, int g, int d);

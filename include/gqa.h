@@ -115,6 +115,32 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * GQE router with its projection: logits = x w_r^T for every token, then the
+ * top-k experts of every KV group and their gates, in one kernel.
+ * The pages have the router examine each token and keep k query-head experts
+ * per group (gist.science explainer of "Grouped Query Experts", section
+ * "Architecture et Routage") without fixing the router's form; this is the
+ * linear reading (one weight row per head, like the attention projections).
+ *   x       [n_tokens, d_model] bf16, device: the tokens' input vectors
+ *           (n_tokens = B*T for a [B, T, d_model] batch).
+ *   w_r     [h, d_model] bf16, device: one row of router weights per head.
+ *   top_k   experts kept per group, 1 <= top_k <= h/g.
+ *   logits  [n_tokens, h] fp32, device, written when not NULL: the scores the
+ *           selection used (accumulated in fp32); they can be passed to
+ *           gqe_routed_prefill as its router_logits.
+ *   topk_idx  [n_tokens, g, top_k] int32, written: kept heads in rank order
+ *           (higher logit first, equal logits by lower head id).
+ *   topk_gate [n_tokens, g, top_k] fp32, written: softmax of the kept logits.
+ * Supported: in_dtype BF16, h <= 64, d_model a multiple of 128.
+ * Errors: GQA_ERR_INVALID_ARG (shape, top_k, null or misaligned pointer),
+ * GQA_ERR_UNSUPPORTED, GQA_ERR_NO_DEVICE, GQA_ERR_HIP.
+ */
+gqa_status gqe_router(const void* x, const void* w_r, int top_k, float* logits,
+                      int32_t* topk_idx, float* topk_gate,
+                      int n_tokens, int d_model, int h, int g,
+                      gqa_dtype in_dtype, void* stream);
+
+/*
  * GQE routed decode: one new token per sequence over a KV cache, with the
  * router of gqe_routed_prefill applied to that token (gist.science explainer
  * of "Grouped Query Experts", section "Architecture et Routage": top-k query

@@ -141,6 +141,35 @@ def test_gqe_decode_rejects(kw, status):
     assert _gqe_decode(**kw) == status
 
 
+def _router(**kw):
+    a = dict(x=P, w=P, k_top=1, lg=P, idx=P, gate=P, n=64, dm=4096, h=32, g=8, i=BF16, stream=None)
+    a.update(kw)
+    return lib.gqe_router(a["x"], a["w"], a["k_top"], a["lg"], a["idx"], a["gate"], a["n"], a["dm"],
+                          a["h"], a["g"], a["i"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_top=0), INVALID),
+    (dict(k_top=5), INVALID),              # more than h/g = 4
+    (dict(h=32, g=5), INVALID),
+    (dict(n=-1), INVALID),
+    (dict(x=None), INVALID),
+    (dict(idx=None), INVALID),
+    (dict(w=P + 8), INVALID),              # misaligned
+    (dict(i=F32), UNSUPPORTED),
+    (dict(dm=200), UNSUPPORTED),           # not a multiple of 128
+    (dict(h=128, g=2), UNSUPPORTED),       # more than 64 heads
+])
+def test_router_rejects(kw, status):
+    assert _router(**kw) == status
+
+
+def test_router_empty_and_optional_logits():
+    assert _router(n=0, x=None) == OK
+    if torch.cuda.device_count() == 0:
+        assert _router(lg=None) == NO_DEVICE   # logits may be NULL
+
+
 def test_gqe_decode_empty_batch_is_ok():
     assert _gqe_decode(B=0, q=None, lg=None) == OK
 

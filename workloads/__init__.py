@@ -30,6 +30,8 @@ __all__ = [
     "torch_dtype",
     "GQE_SWEEP_T",
     "gqe_sweep_points",
+    "router_inputs",
+    "ROUTER_D_MODEL",
 ]
 
 
@@ -93,6 +95,13 @@ def gqe_sweep_points():
             B = max(1, GQE_SWEEP_TOKENS // T)
             pts.append((B, h, g, T, GQE_SWEEP_D, ks, GQE_SWEEP_SEED + T + h))
     return pts
+
+
+# Router projection: the pages give neither the router's form nor the model
+# width; the GQE workload's tokens (B=2, T=4096) are projected from
+# d_model = h * d = 32 * 128 = 4096, the width whose projections give the
+# query heads.
+ROUTER_D_MODEL = 4096
 
 
 def _gen(seed: int, device: str | torch.device) -> torch.Generator:
@@ -171,3 +180,14 @@ def gqe_inputs(B: int, h: int, g: int, T: int, d: int, dtype: str = "bf16",
     k = _normal((B, g, T, d), gen, device, dt)
     v = _normal((B, g, T, d), gen, device, dt)
     return q, k, v, _logits(B, T, h, gen, device, ties)
+
+
+def router_inputs(n_tok: int, d_model: int, h: int, seed: int = 0,
+                  device: str | torch.device = "cpu"):
+    """Router projection inputs: x [n_tok, d_model] ~ N(0,1) and router weights
+    w_r [h, d_model] ~ N(0, 1/d_model), both rounded to bfloat16, so that the
+    logits x w_r^T are about N(0,1) like the GQE workload's router logits."""
+    gen = _gen(seed, device)
+    x = _normal((n_tok, d_model), gen, device, torch.bfloat16)
+    w = torch.randn(h, d_model, generator=gen, device=device, dtype=torch.float32)
+    return x, (w / d_model ** 0.5).to(torch.bfloat16)
