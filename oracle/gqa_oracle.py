@@ -54,6 +54,7 @@ __all__ = [
     "gqe_ref",
     "gqe_decode_ref",
     "gqe_router_ref",
+    "gqe_build_ref",
     "kv_cache_bytes",
     "gqe_active_query_heads",
 ]
@@ -296,6 +297,39 @@ def gqe_router_ref(x, w_r, g: int, top_k: int):
     bound = dm * 2.0 ** -24 * (np.abs(xf) @ np.abs(wf).T)
     idx, gate = gqe_topk_ref(logits.reshape(1, n_tok, h), g, top_k)
     return logits, bound, idx[0], gate[0]
+
+
+def gqe_build_ref(q, q_shared, k, v, logits, top_k: int, shared_kv: int = 0,
+                  causal: bool = True, scale: float | None = None):
+    """GQE layer output as the pages build it -> (concat, wsum, shared, idx, gate).
+
+    gist.science GQE explainer, section "Architecture et Routage", output
+    construction: (1) the outputs of the k experts the router kept in each
+    group are concatenated (hard concatenation); (2) a weighted sum of those
+    outputs with the router probabilities renormalised over the k kept forms
+    an extra slot; (3) one more attention head, shared and always active, is
+    computed for every token. With 16 query heads in 8 groups and k = 1 that
+    is 8 routed + 1 shared = 9 query-attention computations out of 16, so the
+    shared head is one attention over one KV head.
+
+    Readings (the pages leave them open): the shared head reads KV head
+    `shared_kv`; its query q_shared [B,T,d] is an input of its own; the slots
+    are laid out token-major: concat [B,T,g,k,d] (kept experts in rank order,
+    outputs not gated), wsum [B,T,g,d] (one slot per group), shared [B,T,d].
+    """
+    q, qs = _f64(q), _f64(q_shared)
+    B, h, T, d = q.shape
+    g = k.shape[1]
+    idx, gate = gqe_topk_ref(logits, g, top_k)               # [B,T,g,k]
+    dense = gqa_ref(q, k, v, causal=causal, scale=scale)      # [B,h,T,d]
+    concat = np.empty((B, T, g, top_k, d))
+    for b in range(B):
+        for t in range(T):
+            concat[b, t] = dense[b, idx[b, t], t]             # rows of the kept heads
+    wsum = np.einsum("btgk,btgkd->btgd", gate, concat)
+    kv = slice(shared_kv, shared_kv + 1)
+    shared = gqa_ref(qs[:, None], _f64(k)[:, kv], _f64(v)[:, kv], causal=causal, scale=scale)[:, 0]
+    return concat, wsum, shared, idx, gate
 
 
 def kv_cache_bytes(B: int, n_kv: int, T: int, d: int, elt_bytes: int,

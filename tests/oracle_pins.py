@@ -397,6 +397,38 @@ def pin_gqe_router():
     assert idx.shape == (n, g, 2) and gate.shape == (n, g, 2)
 
 
+def pin_gqe_build():
+    """The output build: each group's weighted-sum slot equals the sum over
+    the group's heads of the routed output (gqe_ref: gate x row for kept heads,
+    0 otherwise); with every expert kept the concatenation is the group's dense
+    rows in rank order; the shared head equals torch SDPA of its query against
+    its KV head; g*k routed + 1 shared computations are active (9 of 16 at
+    16 heads, 8 groups, k = 1)."""
+    B, h, g, T, d = 2, 8, 2, 11, 8
+    r = h // g
+    q = _rand((B, h, T, d), 210)
+    qs = _rand((B, T, d), 211)
+    k = _rand((B, g, T, d), 212)
+    v = _rand((B, g, T, d), 213)
+    lg = _tied_logits((B, T, h), 214).astype(np.float32)
+    dense = _sdpa(q, k, v, True)
+    for kk in (1, 2, r):
+        concat, wsum, shared, idx, gate = orc.gqe_build_ref(q, qs, k, v, lg, kk, shared_kv=1)
+        routed, _, _ = orc.gqe_ref(q, k, v, lg, kk, causal=True)
+        for gam in range(g):
+            grp = routed[:, gam * r:(gam + 1) * r].sum(axis=1)        # [B,T,d]
+            assert np.abs(wsum[:, :, gam] - grp).max() < 1e-12
+        if kk == r:
+            for b in range(B):
+                for t in range(T):
+                    for gam in range(g):
+                        ref = dense[b, idx[b, t, gam], t]
+                        assert np.abs(concat[b, t, gam] - ref).max() < 1e-12
+    sh = _sdpa(qs[:, None], k[:, 1:2], v[:, 1:2], True)[:, 0]
+    assert np.abs(shared - sh).max() < 1e-12
+    assert orc.gqe_active_query_heads(8, 1) == 9
+
+
 # --------------------------------------------------------------------------
 # Accounting printed on the pages
 # --------------------------------------------------------------------------
@@ -443,6 +475,7 @@ PINS = [
     pin_gqe_structure,
     pin_gqe_decode,
     pin_gqe_router,
+    pin_gqe_build,
     pin_kv_cache_law,
     pin_gqe_active_count,
 ]

@@ -114,6 +114,17 @@ def _router_dropped_feature(x, w_r, g, top_k):   # the last input feature ignore
     return _orig["gqe_router_ref"](np.asarray(x)[:, :-1], np.asarray(w_r)[:, :-1], g, top_k)
 
 
+def _build_wrong_shared_kv(q, q_shared, k, v, logits, top_k, shared_kv=0, causal=True, scale=None):
+    return _orig["gqe_build_ref"](q, q_shared, k, v, logits, top_k, (shared_kv + 1) % k.shape[1],
+                                  causal, scale)
+
+
+def _build_wsum_unrenormalised(q, q_shared, k, v, logits, top_k, shared_kv=0, causal=True, scale=None):
+    concat, wsum, shared, idx, gate = _orig["gqe_build_ref"](q, q_shared, k, v, logits, top_k,
+                                                             shared_kv, causal, scale)
+    return concat, wsum * 0.5, shared, idx, gate
+
+
 def _active_no_shared(g, top_k, shared=1):
     return g * top_k
 
@@ -136,6 +147,8 @@ MUTATIONS = {
     "gqe_decode/gate_dropped": ("gqe_decode_ref", _gqe_decode_no_gate),
     "gqe_decode/unselected_not_zero": ("gqe_decode_ref", _gqe_decode_no_zero),
     "gqe_router/dropped_feature": ("gqe_router_ref", _router_dropped_feature),
+    "gqe_build/wrong_shared_kv": ("gqe_build_ref", _build_wrong_shared_kv),
+    "gqe_build/wsum_scaled": ("gqe_build_ref", _build_wsum_unrenormalised),
     "kv_cache_bytes/no_factor_two": ("kv_cache_bytes", _kv_bytes_no_two),
     "kv_head_of/strided": ("kv_head_of", _kv_head_strided),
     "active_heads/no_shared": ("gqe_active_query_heads", _active_no_shared),
