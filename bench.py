@@ -321,6 +321,17 @@ def main():
                 return stats(tm.ms())["median_ms"]
 
             dense_ms = timed(lambda: gq.gqa_prefill(q, k, v, causal=True, out=out))
+            if h == 16:
+                # the pages' configuration: k=1 routed experts in 8 groups plus the
+                # shared head (9 of 16 query heads), full output build
+                qs = torch.randn(B, T, d, device=dev).to(torch.bfloat16)
+                ms = timed(lambda: gq.gqe_prefill_build(q, qs, k, v, lg, 1, shared_kv=0))
+                gsweep.append(dict(B=B, h=h, g=g, T=T, d=d, top_k=1, build="concat+wsum+shared",
+                                   routed_us=ms * 1e3, dense_us=dense_ms * 1e3,
+                                   speedup=dense_ms / ms))
+                log(f"gqe build h={h} g={g} T={T} B={B} k=1 +shared: {ms*1e3:.1f} us, "
+                    f"speed-up {dense_ms/ms:.2f}")
+                del qs
             for kk in ks:
                 ms = timed(lambda: gq.gqe_routed_prefill(q, k, v, lg, kk, causal=True, out=out))
                 fl = dense_flops * kk / (h // g)

@@ -10,6 +10,8 @@ this package only marshals torch tensors into its entry points:
   per token, dense K/V.
 * :func:`gqe_routed_decode` -- GQE routing applied to one decode step.
 * :func:`gqe_router` -- the router's projection x W_r^T fused with the top-k.
+* :func:`gqe_prefill_build` -- the GQE layer output: kept experts concatenated,
+  their weighted-sum slot and the shared head.
 
 torch provides device memory and the stream; every step of the computation
 runs in the library's kernels. Importing the package fails loudly when the
@@ -24,6 +26,7 @@ from ._binding import (  # noqa: F401
     gqa_decode_workspace_bytes,
     gqa_kv_cache_bytes,
     gqa_prefill,
+    gqe_prefill_build,
     gqe_routed_decode,
     gqe_routed_prefill,
     gqe_router,

@@ -53,6 +53,9 @@ def _load():
     lib.gqe_routed_decode.restype = i32
     lib.gqe_routed_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32,
                                       i32, i32, i32, f32, vp, sz, vp]
+    lib.gqe_prefill_build.restype = i32
+    lib.gqe_prefill_build.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, i32, i32,
+                                      i32, i32, i32, i32, i32, f32, i32, vp]
     lib.gqe_router.restype = i32
     lib.gqe_router.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     lib.gqa_kv_cache_bytes.restype = ctypes.c_uint64
@@ -272,3 +275,35 @@ def gqe_router(x, w_r, g: int, top_k: int, return_logits: bool = True):
                          gate.data_ptr(), n_tok, d_model, h, int(g), _dt(x, "x"), _stream(dev))
     _check("gqe_router", st)
     return logits, idx, gate
+
+
+def gqe_prefill_build(q, q_shared, k, v, router_logits, top_k: int, shared_kv: int = 0,
+                      causal: bool = True, scale: float | None = None, out_dtype=None):
+    """GQE output build. q [B,h,T,d], q_shared [B,T,d], k/v [B,g,T,d], router_logits
+    [B,T,h] -> (concat [B,T,g,k,d], wsum [B,T,g,d], shared [B,T,d], idx, gate)."""
+    dev = _dev(q, q_shared, k, v, router_logits)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q [B,h,T,d] and k, v [B,g,T,d]")
+    B, h, T, d = q.shape
+    g = k.shape[1]
+    if k.shape[0] != B or k.shape[2:] != (T, d) or q_shared.shape != (B, T, d):
+        raise ValueError("k/v or q_shared shape does not match q")
+    if router_logits.dtype != torch.float32 or router_logits.shape != (B, T, h):
+        raise ValueError("router_logits must be float32 [B,T,h]")
+    if k.dtype != q.dtype or v.dtype != q.dtype or q_shared.dtype != q.dtype:
+        raise TypeError("q, q_shared, k and v must share one dtype")
+    out_dtype = out_dtype or q.dtype
+    kk = max(int(top_k), 1)
+    concat = torch.empty((B, T, g, kk, d), dtype=out_dtype, device=dev)
+    wsum = torch.empty((B, T, g, d), dtype=out_dtype, device=dev)
+    shared = torch.empty((B, T, d), dtype=out_dtype, device=dev)
+    idx = torch.empty((B, T, g, kk), dtype=torch.int32, device=dev)
+    gate = torch.empty((B, T, g, kk), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = _lib.gqe_prefill_build(q.data_ptr(), q_shared.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                router_logits.data_ptr(), int(top_k), int(shared_kv),
+                                concat.data_ptr(), wsum.data_ptr(), shared.data_ptr(),
+                                idx.data_ptr(), gate.data_ptr(), B, h, g, T, d, _dt(q, "q"),
+                                _DT[out_dtype], scale, int(bool(causal)), _stream(dev))
+    _check("gqe_prefill_build", st)
+    return concat, wsum, shared, idx, gate

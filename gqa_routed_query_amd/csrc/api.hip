@@ -209,6 +209,55 @@ gqa_status gqe_routed_decode(const void* q, const void* k_cache, const void* v_c
   return hip_status(gqa::launch_decode(p, st), "gqe routed decode launch");
 }
 
+gqa_status gqe_prefill_build(const void* q, const void* q_shared, const void* k, const void* v,
+                             const float* router_logits, int top_k, int shared_kv, void* out_concat,
+                             void* out_wsum, void* out_shared, int32_t* topk_idx, float* topk_gate,
+                             int B, int h, int g, int T, int d, gqa_dtype in_dtype,
+                             gqa_dtype out_dtype, float scale, int causal, void* stream) {
+  g_last_error[0] = '\0';
+  gqa_status s = check_prefill_shape(q, k, v, out_concat, B, h, g, T, d, in_dtype, out_dtype, scale, causal);
+  if (s != GQA_OK) return s;
+  const int r = h / g;
+  if (top_k < 1 || top_k > r) return fail(GQA_ERR_INVALID_ARG, "top_k=%d must be in [1, h/g=%d]", top_k, r);
+  if (shared_kv < 0 || shared_kv >= g) return fail(GQA_ERR_INVALID_ARG, "shared_kv=%d must be in [0, g=%d)", shared_kv, g);
+  if (in_dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "the GQE output build takes bf16 inputs");
+  if (!gqa::attn_bf16_supports(d)) return fail(GQA_ERR_UNSUPPORTED, "the GQE output build supports d in {64, 128}, got %d", d);
+  if (r > 64) return fail(GQA_ERR_UNSUPPORTED, "routing supports h/g <= 64, got %d", r);
+  if (B == 0 || T == 0) return GQA_OK;
+  if (!q_shared || !router_logits || !out_wsum || !out_shared || !topk_idx || !topk_gate)
+    return fail(GQA_ERR_INVALID_ARG, "null q_shared, router_logits, output, topk_idx or topk_gate pointer");
+  if (!aligned16(q_shared) || !aligned16(out_wsum) || !aligned16(out_shared))
+    return fail(GQA_ERR_INVALID_ARG, "q_shared and the outputs must be 16-byte aligned");
+  if ((s = check_device()) != GQA_OK) return s;
+  auto st = static_cast<hipStream_t>(stream);
+  // 1. router: kept experts and gates per (token, group)
+  gqa::RouterParams rp{router_logits, topk_idx, topk_gate, B, T, h, g, top_k};
+  if ((s = hip_status(gqa::launch_router(rp, st), "gqe build router launch")) != GQA_OK) return s;
+  // 2. kept experts' rows, ungated, into out_concat [B, T, g, k, d]
+  gqa::AttnParams p{};
+  p.q = q; p.k = k; p.v = v; p.out = out_concat;
+  p.idx = topk_idx;
+  p.gate = topk_gate;
+  p.B = B; p.h = h; p.g = g; p.T = T; p.d = d;
+  p.R = top_k;
+  p.scale = scale;
+  p.causal = causal;
+  p.out_bf16 = out_dtype == GQA_BF16;
+  p.out_slots = 1;
+  p.o_b = (size_t)T * g * top_k * d;
+  p.o_h = d;
+  p.o_t = (size_t)g * top_k * d;
+  // 3. the shared head, one query per token on KV head shared_kv, as extra
+  //    problems of the same launch (its row tiles are scheduled with the routed ones)
+  p.q_shared = q_shared;
+  p.out_shared = out_shared;
+  p.shared_kv = shared_kv;
+  if ((s = hip_status(gqa::launch_attn_bf16(p, st), "gqe build attention launch")) != GQA_OK) return s;
+  // 4. the weighted-sum slot of every (token, group)
+  gqa::WsumParams wp{out_concat, topk_gate, out_wsum, (long long)B * T * g, top_k, d, out_dtype == GQA_BF16};
+  return hip_status(gqa::launch_wsum(wp, st), "gqe build weighted-sum launch");
+}
+
 gqa_status gqe_router(const void* x, const void* w_r, int top_k, float* logits, int32_t* topk_idx,
                       float* topk_gate, int n_tokens, int d_model, int h, int g, gqa_dtype in_dtype,
                       void* stream) {

@@ -72,6 +72,17 @@ struct KArgs {
   int BG;
   float c;  // scale * log2(e)
   int causal, out_bf16, zero_unselected;
+  int out_slots;  // 1: output row of (token, group, slot) is slot gam*R + slot, not its head; no gate
+  // Element strides: q row (b, head, t) at b*q_b + head*q_h + t*D; the K/V rows
+  // of (b, gam) start at b*kv_b + gam*kv_g; output row (b, o, t) at
+  // b*o_b + o*o_h + t*o_t, o being the head or the slot.
+  size_t q_b, q_h, kv_b, kv_g, o_b, o_h, o_t;
+  // Problems bg >= BG_main (when q_sh is set): the shared head of batch
+  // bg - BG_main, one query row per token (q_sh, out_sh [B, T, D]) on KV head sh_kv.
+  int BG_main;
+  const uint16_t* q_sh;
+  void* out_sh;
+  int sh_kv;
 };
 
 // Zero the output rows of heads the router did not keep, for the tokens whose
@@ -96,7 +107,7 @@ __device__ void zero_unselected_rows(const KArgs& a, int b, int gam, int row0, i
     bool kept = false;
     for (int j = 0; j < R; ++j) kept |= (sel[j] == head);
     if (kept) continue;
-    const size_t off = ((size_t)(b * a.h + head) * a.T + t) * D + ch * 8;
+    const size_t off = b * a.o_b + head * a.o_h + t * a.o_t + ch * 8;
     const uint4 z = {0u, 0u, 0u, 0u};
     if (a.out_bf16) {
       *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + off) = z;
@@ -119,30 +130,36 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(KArgs a) {
   const int bid = blockIdx.x;
   const int bg = bid % a.BG;
   const int tile = a.causal ? (a.n_row_tiles - 1 - bid / a.BG) : (bid / a.BG);
-  const int b = bg / a.g;
-  const int gam = bg - b * a.g;
+  // The shared head's problem (uniform per block; only routed launches carry one).
+  const bool shared = ROUTED && bg >= a.BG_main;
+  const int b = shared ? bg - a.BG_main : bg / a.g;
+  const int gam = shared ? a.sh_kv : bg - b * a.g;
+  const int R = shared ? 1 : a.R;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hq = lane >> 5;  // which half of the reduction dim / key quad this lane holds
-  const int n_rows = a.T * a.R;
+  const int n_rows = a.T * R;
   const int row0 = tile * kRowsPerBlock;
+  if (row0 >= n_rows) return;  // a shared-head problem has T rows, fewer than the routed ones when k > 1
 
-  if (ROUTED && a.zero_unselected) zero_unselected_rows<D, W>(a, b, gam, row0, n_rows);
+  if (ROUTED && a.zero_unselected && !shared) zero_unselected_rows<D, W>(a, b, gam, row0, n_rows);
 
   // This lane's attention row.
   const int rho = row0 + wave * 32 + l32;
   const bool row_valid = rho < n_rows;
   const int rho_c = row_valid ? rho : n_rows - 1;
-  const int t_row = rho_c / a.R;
-  const int slot = rho_c - t_row * a.R;
+  const int t_row = rho_c / R;
+  const int slot = rho_c - t_row * R;
   int head;
   float gate = 1.0f;
-  if (ROUTED) {
+  if (shared) {
+    head = 0;
+  } else if (ROUTED) {
     const size_t o = ((size_t)(b * a.T + t_row) * a.g + gam) * a.R + slot;
     head = a.idx[o];
-    gate = a.gate[o];
+    gate = a.out_slots ? 1.0f : a.gate[o];
   } else {
     head = gam * a.r + slot;
   }
@@ -150,9 +167,9 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(KArgs a) {
   // Token range of this wave and of the block (uniform values).
   const int wrow0 = row0 + wave * 32;
   const bool wave_has_rows = wrow0 < n_rows;
-  const int wt_lo = min(wrow0, n_rows - 1) / a.R;
-  const int wt_hi = (min(wrow0 + 31, n_rows - 1)) / a.R;
-  const int t_last = (min(row0 + kRowsPerBlock, n_rows) - 1) / a.R;
+  const int wt_lo = min(wrow0, n_rows - 1) / R;
+  const int wt_hi = (min(wrow0 + 31, n_rows - 1)) / R;
+  const int t_last = (min(row0 + kRowsPerBlock, n_rows) - 1) / R;
   const int n_keys = a.causal ? t_last + 1 : a.T;
   const int n_tiles = div_up(n_keys, kBN);
 
@@ -160,13 +177,14 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(KArgs a) {
   // [hq*D/2, hq*D/2 + D/2); step st uses 8 of them.
   bf16x8 qf[D / 16];
   {
-    const uint16_t* qrow = a.q + ((size_t)(b * a.h + head) * a.T + t_row) * D + hq * (D / 2);
+    const uint16_t* qrow = (shared ? a.q_sh + (size_t)b * a.T * D : a.q + b * a.q_b + head * a.q_h) +
+                           (size_t)t_row * D + hq * (D / 2);
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 8 * st);
   }
 
-  const uint16_t* kbase = a.k + (size_t)bg * a.T * D;
-  const uint16_t* vbase = a.v + (size_t)bg * a.T * D;
+  const uint16_t* kbase = a.k + b * a.kv_b + gam * a.kv_g;
+  const uint16_t* vbase = a.v + b * a.kv_b + gam * a.kv_g;
   uint4 rk[L::kLoads], rv[L::kLoads];
   auto load_tile = [&](int kt) {
 #pragma unroll
@@ -309,7 +327,10 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(KArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (row_valid) {
     const float inv = gate / l_tot;
-    const size_t obase = ((size_t)(b * a.h + head) * a.T + t_row) * D + 4 * hq;
+    const int oslot = a.out_slots ? gam * a.R + slot : head;
+    void* const outp = shared ? a.out_sh : a.out;
+    const size_t obase = shared ? ((size_t)b * a.T + t_row) * D + 4 * hq
+                                : b * a.o_b + oslot * a.o_h + t_row * a.o_t + 4 * hq;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -319,9 +340,9 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(KArgs a) {
         const float x2 = o[db][4 * i4 + 2] * inv, x3 = o[db][4 * i4 + 3] * inv;
         if (a.out_bf16) {
           uint2 w = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) = w;
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(outp) + off) = w;
         } else {
-          *reinterpret_cast<float4*>(static_cast<float*>(a.out) + off) = make_float4(x0, x1, x2, x3);
+          *reinterpret_cast<float4*>(static_cast<float*>(outp) + off) = make_float4(x0, x1, x2, x3);
         }
       }
   }
@@ -352,11 +373,25 @@ hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
   a.T = p.T;
   a.R = p.R;
   a.r = p.h / p.g;
-  a.BG = p.B * p.g;
+  a.BG_main = p.B * p.g;
+  a.q_sh = static_cast<const uint16_t*>(p.q_shared);
+  a.out_sh = p.out_shared;
+  a.sh_kv = p.shared_kv;
+  if (p.q_shared && !p.idx) return hipErrorInvalidValue;  // a shared head rides on a routed launch
+  a.BG = a.BG_main + (p.q_shared ? p.B : 0);
   a.c = p.scale * kLog2e;
   a.causal = p.causal;
   a.out_bf16 = p.out_bf16;
   a.zero_unselected = p.zero_unselected;
+  a.out_slots = p.out_slots;
+  const size_t TD = (size_t)p.T * D;
+  a.q_b = p.q_b ? p.q_b : (size_t)p.h * TD;
+  a.q_h = TD;
+  a.kv_b = p.kv_b ? p.kv_b : (size_t)p.g * TD;
+  a.kv_g = TD;
+  a.o_b = p.o_b ? p.o_b : (size_t)p.h * TD;
+  a.o_h = p.o_h ? p.o_h : TD;
+  a.o_t = p.o_t ? p.o_t : D;
   int n_cu = 256, dev = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)

@@ -212,6 +212,8 @@ hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
 bool attn_f32_supports(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream) {
+  if (p.out_slots || p.q_b || p.kv_b || p.o_b || p.o_h || p.o_t || p.q_shared)
+    return hipErrorInvalidValue;  // default layout only
   switch (p.d) {
     case 16: return launch_d<16>(p, stream);
     case 32: return launch_d<32>(p, stream);

@@ -27,6 +27,16 @@ struct AttnParams {
   int causal;           // 0 or 1
   int out_bf16;         // 1: bf16 output, 0: fp32 output
   int zero_unselected;  // routed only: write zeros to the rows of unselected heads
+  // Layout overrides (bf16 kernel only; 0 keeps the [B,h,T,d] / [B,g,T,d] default):
+  int out_slots;        // routed: row (t, gam, j) goes to output slot gam*R + j, ungated
+  size_t q_b;           // elements between batches of q
+  size_t kv_b;          // elements between batches of k and v
+  size_t o_b, o_h, o_t; // output strides: batch, head (or slot), token
+  // Shared head run in the same launch (bf16 kernel only; null: none): one
+  // query row per token, q_shared / out_shared [B, T, d], on KV head shared_kv.
+  const void* q_shared;
+  void* out_shared;
+  int shared_kv;
 };
 
 struct RouterParams {
@@ -34,6 +44,14 @@ struct RouterParams {
   int32_t* idx;         // [B, T, g, k]
   float* gate;          // [B, T, g, k]
   int B, T, h, g, k;
+};
+
+struct WsumParams {
+  const void* concat;   // [n, k, d] rows of the kept experts (out dtype)
+  const float* gate;    // [n, k]
+  void* wsum;           // [n, d]
+  long long n;          // (batch, token, group) triples
+  int k, d, bf16;
 };
 
 struct RouterProjParams {
@@ -66,6 +84,7 @@ hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
 hipError_t launch_router(const RouterParams& p, hipStream_t stream);
 hipError_t launch_router_proj(const RouterProjParams& p, hipStream_t stream);
+hipError_t launch_wsum(const WsumParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
 // Head dims with a bf16 MFMA prefill kernel / an fp32 kernel / a decode kernel.

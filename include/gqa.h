@@ -115,6 +115,38 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * GQE layer output as the pages build it (gist.science explainer of "Grouped
+ * Query Experts", section "Architecture et Routage", output construction):
+ * the outputs of the k experts kept in every group, concatenated; a weighted
+ * sum of them with the router probabilities renormalised over the k kept; and
+ * one more head, shared and always active, computed for every token. At 16
+ * query heads in 8 groups with k = 1 that is 9 query-attention computations
+ * of 16. Readings where the pages are silent: the shared head reads KV head
+ * shared_kv and has a query of its own; the outputs are token-major.
+ *   q [B, h, T, d], k/v [B, g, T, d], router_logits [B, T, h]: as for
+ *           gqe_routed_prefill; in_dtype BF16 only.
+ *   q_shared [B, T, d] in_dtype: the shared head's queries.
+ *   top_k   experts kept per group, 1 <= top_k <= h/g <= 64.
+ *   shared_kv  KV head read by the shared head, 0 <= shared_kv < g.
+ *   out_concat [B, T, g, top_k, d] out_dtype, written: the attention rows of
+ *           the kept heads (not gated), groups in order, experts in rank order.
+ *   out_wsum [B, T, g, d] out_dtype, written: sum over j of gate_j * row_j,
+ *           formed from out_concat as stored (rounded to out_dtype).
+ *   out_shared [B, T, d] out_dtype, written: the shared head's attention.
+ *   topk_idx / topk_gate [B, T, g, top_k]: as for gqe_routed_prefill.
+ * Supported: d in {64, 128}. Errors as for gqe_routed_prefill, plus
+ * GQA_ERR_INVALID_ARG for shared_kv outside [0, g) and GQA_ERR_UNSUPPORTED
+ * for fp32 inputs.
+ */
+gqa_status gqe_prefill_build(const void* q, const void* q_shared, const void* k, const void* v,
+                             const float* router_logits, int top_k, int shared_kv,
+                             void* out_concat, void* out_wsum, void* out_shared,
+                             int32_t* topk_idx, float* topk_gate,
+                             int B, int h, int g, int T, int d,
+                             gqa_dtype in_dtype, gqa_dtype out_dtype,
+                             float scale, int causal, void* stream);
+
+/*
  * GQE router with its projection: logits = x w_r^T for every token, then the
  * top-k experts of every KV group and their gates, in one kernel.
  * The pages have the router examine each token and keep k query-head experts

@@ -170,6 +170,31 @@ def test_router_empty_and_optional_logits():
         assert _router(lg=None) == NO_DEVICE   # logits may be NULL
 
 
+def _build(**kw):
+    a = dict(q=P, qs=P, k=P, v=P, lg=P, k_top=1, skv=0, oc=P, ow=P, osh=P, idx=P, gate=P, B=1, h=16,
+             g=8, T=64, d=128, i=BF16, o=BF16, scale=0.088, causal=1, stream=None)
+    a.update(kw)
+    return lib.gqe_prefill_build(a["q"], a["qs"], a["k"], a["v"], a["lg"], a["k_top"], a["skv"],
+                                 a["oc"], a["ow"], a["osh"], a["idx"], a["gate"], a["B"], a["h"],
+                                 a["g"], a["T"], a["d"], a["i"], a["o"], a["scale"], a["causal"],
+                                 a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_top=0), INVALID),
+    (dict(k_top=3), INVALID),              # more than h/g = 2
+    (dict(skv=8), INVALID),
+    (dict(skv=-1), INVALID),
+    (dict(qs=None), INVALID),
+    (dict(osh=None), INVALID),
+    (dict(ow=P + 4), INVALID),             # misaligned
+    (dict(i=F32, d=16), UNSUPPORTED),
+    (dict(d=32), UNSUPPORTED),
+])
+def test_gqe_build_rejects(kw, status):
+    assert _build(**kw) == status
+
+
 def test_gqe_decode_empty_batch_is_ok():
     assert _gqe_decode(B=0, q=None, lg=None) == OK
 
@@ -180,6 +205,7 @@ def test_valid_calls_report_no_device():
     assert _decode() == NO_DEVICE
     assert _gqe() == NO_DEVICE
     assert _gqe_decode() == NO_DEVICE
+    assert _build() == NO_DEVICE
 
 
 def test_kv_cache_bytes_matches_oracle_law():
