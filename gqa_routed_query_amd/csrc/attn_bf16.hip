@@ -29,11 +29,17 @@
 //    lanes (l and l^32) -- one cross-lane max per tile, sums combined once.
 //  * K tiles are read from LDS with 16-byte reads in the A-operand layout; V
 //    stays row-major in LDS and is transposed by ds_read_b64_tr_b16.
-//  * Double-buffered LDS: the next tile's global loads are in flight while the
-//    current tile is multiplied; one barrier per tile.
+//  * K/V tiles reach LDS by DMA (global_load_lds_dwordx4, no registers), double
+//    buffered: the next tile is in flight while the current one is multiplied;
+//    one barrier per tile.
+//  * Q comes in and the output goes out through a per-wave LDS region, so
+//    both move whole rows per instruction; read straight from HBM in the
+//    fragment layouts, each instruction would touch 16 bytes of 32 rows.
 //  * Causal grids are issued heaviest-first; (batch, group) is the fastest
 //    varying part of the block index, so with B*g a multiple of 8 all tiles of
 //    one group land on one XCD and share its L2.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -44,8 +50,8 @@ namespace {
 // large grids, and 8 waves with 64-key tiles (two waves per SIMD, half the
 // per-tile overhead) when a 12-wave grid would leave compute units without
 // two workgroups' worth of work (short routed problems).
-constexpr int kWavesLarge = 12, kBNLarge = 32;
-constexpr int kWavesSmall = 8, kBNSmall = 64;
+constexpr int kWavesLarge = 12, kBNLarge = 32, kOccLarge = 3;
+constexpr int kWavesSmall = 8, kBNSmall = 64, kOccSmall = 2;
 constexpr float kRescale = 8.0f;                      // lazy-rescale threshold, log2 units
 
 template <int D, int W, int kBN>
@@ -53,11 +59,18 @@ struct Tile {
   static constexpr int kThreads = W * 64;
   static constexpr int kPitch = D + 8;    // 16-byte pad: A-operand reads of 16 rows hit distinct banks
   static constexpr int vPitch = D + 32;   // 64-byte pad: transposing reads of 4 rows hit distinct banks
-  static constexpr int kElems = kBN * kPitch;
-  static constexpr int vElems = kBN * vPitch;
-  static constexpr int kCPR = D / 8;      // 16-byte chunks per row
-  static constexpr int kChunks = kBN * kCPR;
-  static constexpr int kLoads = (kChunks + kThreads - 1) / kThreads;
+  static constexpr int kCPR = D / 8;      // 16-byte granules of data per row
+  // Staging by DMA: one global_load_lds_dwordx4 fills 64 consecutive 16-byte
+  // LDS granules, so a padded tile is filled granule by granule, pad granules
+  // included (they receive a copy of an in-row granule and are never read).
+  static constexpr int kGPR = kPitch / 8;  // granules per K row, pad included
+  static constexpr int vGPR = vPitch / 8;  // granules per V row, pad included
+  static constexpr int kDmaK = (kBN * kGPR + 63) / 64;
+  static constexpr int kDmaV = (kBN * vGPR + 63) / 64;
+  static constexpr int kDma = kDmaK + kDmaV;
+  static constexpr int kMine = (kDma + W - 1) / W;  // DMA instructions per wave, at most
+  static constexpr int kElems = kDmaK * 512;        // bf16 elements per K buffer
+  static constexpr int vElems = kDmaV * 512;
 };
 
 struct KArgs {
@@ -119,13 +132,23 @@ __device__ void zero_unselected_rows(const KArgs& a, int b, int gam, int row0, i
   }
 }
 
-template <int D, int W, int kBN, bool ROUTED>
-__global__ __launch_bounds__(W * 64) void attn_bf16_kernel(KArgs a) {
+template <int D, int W, int kBN, int OCC, bool ROUTED>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) void attn_bf16_kernel(KArgs a) {
   using L = Tile<D, W, kBN>;
   constexpr int kThreads = W * 64, kRowsPerBlock = W * 32;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (L::kElems + L::vElems)];
-  uint16_t* Ks = smem;
-  uint16_t* Vs = smem + 2 * L::kElems;
+  // One array per buffer: with the buffer fixed at compile time, the compiler
+  // can tell that reads of one buffer do not alias the DMA into the other and
+  // adds no wait for the DMA before them.
+  __shared__ __attribute__((aligned(16))) uint16_t K0[L::kElems], K1[L::kElems];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[L::vElems], V1[L::vElems];
+  // Per-wave staging of the wave's 32 rows (padded pitch kPitch): Q on the way
+  // in, the output on the way out, so that both move whole rows per
+  // instruction instead of 16 bytes of 32 different rows.
+  constexpr int kQDma = (32 * L::kGPR + 63) / 64;
+  constexpr int kQElems = kQDma * 512;
+  __shared__ __attribute__((aligned(16))) uint16_t QO[W * kQElems];
+  // Per-wave table of the wave's 32 rows: token, head, slot, gate.
+  __shared__ int4 rowtab[W * 32];
 
   const int bid = blockIdx.x;
   const int bg = bid % a.BG;
@@ -146,23 +169,32 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(KArgs a) {
 
   if (ROUTED && a.zero_unselected && !shared) zero_unselected_rows<D, W>(a, b, gam, row0, n_rows);
 
-  // This lane's attention row.
+  // Attention row rho (< n_rows): token, slot, head (a routed row's head is
+  // the router's pick) and gate.
+  struct RowInfo {
+    int t, slot, head;
+    float gate;
+  };
+  auto row_info = [&](int rho) {
+    RowInfo ri;
+    ri.t = rho / R;
+    ri.slot = rho - ri.t * R;
+    ri.gate = 1.0f;
+    if (shared) {
+      ri.head = 0;
+    } else if (ROUTED) {
+      const size_t o = ((size_t)(b * a.T + ri.t) * a.g + gam) * a.R + ri.slot;
+      ri.head = a.idx[o];
+      ri.gate = a.out_slots ? 1.0f : a.gate[o];
+    } else {
+      ri.head = gam * a.r + ri.slot;
+    }
+    return ri;
+  };
+
+  // This lane's attention row (the last row stands in for rows past the end).
   const int rho = row0 + wave * 32 + l32;
-  const bool row_valid = rho < n_rows;
-  const int rho_c = row_valid ? rho : n_rows - 1;
-  const int t_row = rho_c / R;
-  const int slot = rho_c - t_row * R;
-  int head;
-  float gate = 1.0f;
-  if (shared) {
-    head = 0;
-  } else if (ROUTED) {
-    const size_t o = ((size_t)(b * a.T + t_row) * a.g + gam) * a.R + slot;
-    head = a.idx[o];
-    gate = a.out_slots ? 1.0f : a.gate[o];
-  } else {
-    head = gam * a.r + slot;
-  }
+  const int t_row = min(rho, n_rows - 1) / R;
 
   // Token range of this wave and of the block (uniform values).
   const int wrow0 = row0 + wave * 32;
@@ -173,43 +205,67 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(KArgs a) {
   const int n_keys = a.causal ? t_last + 1 : a.T;
   const int n_tiles = div_up(n_keys, kBN);
 
-  // Q^T fragments: B operand of S^T = K Q^T. Lane half hq holds d in
-  // [hq*D/2, hq*D/2 + D/2); step st uses 8 of them.
-  bf16x8 qf[D / 16];
-  {
-    const uint16_t* qrow = (shared ? a.q_sh + (size_t)b * a.T * D : a.q + b * a.q_b + head * a.q_h) +
-                           (size_t)t_row * D + hq * (D / 2);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint16_t* const QOw = QO + wave_u * kQElems;
+  int4* const tab = rowtab + wave_u * 32;
+  // Each lane resolves its own row once (rows past the end stand in as the
+  // last row); lanes that move other rows read them from the table.
+  if (hq == 0) {
+    const RowInfo ri = row_info(min(rho, n_rows - 1));
+    tab[l32] = make_int4(ri.t, ri.head, ri.slot, __float_as_int(ri.gate));
+  }
+  __syncthreads();
+  // The wave's 32 Q rows into QOw by DMA, granule by granule as for K (pad
+  // granules receive a copy of granule 0).
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 8 * st);
+  for (int j = 0; j < kQDma; ++j) {
+    const int p = j * 64 + lane;
+    int row = p / L::kGPR, gr = p - row * L::kGPR;
+    if (row > 31) row = 31;
+    if (gr >= L::kCPR) gr = 0;
+    const int4 ri = tab[row];
+    const uint16_t* src = (shared ? a.q_sh + (size_t)b * a.T * D : a.q + b * a.q_b + (size_t)ri.y * a.q_h) +
+                          (size_t)ri.x * D + gr * 8;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(QOw + j * 512), 16, 0, 0);
   }
 
   const uint16_t* kbase = a.k + b * a.kv_b + gam * a.kv_g;
   const uint16_t* vbase = a.v + b * a.kv_b + gam * a.kv_g;
-  uint4 rk[L::kLoads], rv[L::kLoads];
-  auto load_tile = [&](int kt) {
+  // Byte offsets (from the tile's first key row) that this lane loads for the
+  // wave's DMA instructions j = wave + W*i: K granules first, then V.
+  uint32_t dma_off[L::kMine];
 #pragma unroll
-    for (int i = 0; i < L::kLoads; ++i) {
-      const int c = tid + i * kThreads;
-      const int key = kt * kBN + c / L::kCPR;
-      const int col = (c % L::kCPR) * 8;
-      if (c < L::kChunks && key < a.T) {
-        rk[i] = *reinterpret_cast<const uint4*>(kbase + (size_t)key * D + col);
-        rv[i] = *reinterpret_cast<const uint4*>(vbase + (size_t)key * D + col);
-      } else {
-        rk[i] = make_uint4(0u, 0u, 0u, 0u);  // keys past T: finite zeros, masked below
-        rv[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = 0; i < L::kMine; ++i) {
+    const int j = wave_u + W * i;
+    const bool isk = j < L::kDmaK;
+    const int gpr = isk ? L::kGPR : L::vGPR;
+    const int p = (isk ? j : j - L::kDmaK) * 64 + lane;
+    int row = p / gpr, gr = p - row * gpr;
+    if (row >= kBN) row = kBN - 1;  // rounding slack after the last row
+    if (gr >= L::kCPR) gr = 0;      // pad granule
+    dma_off[i] = (uint32_t)(row * D + gr * 8) * 2u;
+  }
+  // Start the DMA of key tile kt into buffer buf. Keys past T (last tile only)
+  // are clamped to key T-1: finite values that the mask discards.
+  auto issue_tile = [&](int kt, auto buf) {
+    uint16_t* const Kb = buf.value ? K1 : K0;
+    uint16_t* const Vb = buf.value ? V1 : V0;
+    const int key0 = kt * kBN;
+    const bool full = key0 + kBN <= a.T;
+#pragma unroll
+    for (int i = 0; i < L::kMine; ++i) {
+      const int j = wave_u + W * i;
+      if (j >= L::kDma) break;
+      const bool isk = j < L::kDmaK;
+      uint32_t off = dma_off[i];
+      if (!full) {
+        const int last = a.T - 1 - key0;  // >= 0: a tile is issued only if key0 < T
+        if ((int)(off / (2 * D)) > last) off = (uint32_t)last * (2 * D) + (off & (2 * D - 1));
       }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < L::kLoads; ++i) {
-      const int c = tid + i * kThreads;
-      if (c >= L::kChunks) continue;
-      const int row = c / L::kCPR;
-      const int col = (c % L::kCPR) * 8;
-      *reinterpret_cast<uint4*>(Ks + buf * L::kElems + row * L::kPitch + col) = rk[i];
-      *reinterpret_cast<uint4*>(Vs + buf * L::vElems + row * L::vPitch + col) = rv[i];
+      const char* base = reinterpret_cast<const char*>((isk ? kbase : vbase) + (size_t)key0 * D);
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(base + off);
+      uint16_t* dst = isk ? Kb + j * 512 : Vb + (j - L::kDmaK) * 512;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
   };
 
@@ -231,20 +287,32 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(KArgs a) {
   const int tr_col = 16 * (grp & 1) + 4 * (i16 & 3);
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  load_tile(0);
-  store_tile(0);
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  issue_tile(0, B0{});
   __syncthreads();
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_tiles) load_tile(kt + 1);
+  // Q^T fragments: B operand of S^T = K Q^T. Lane half hq holds d in
+  // [hq*D/2, hq*D/2 + D/2); step st uses 8 of them.
+  bf16x8 qf[D / 16];
+  {
+    const uint16_t* qrow = QOw + l32 * L::kPitch + hq * (D / 2);
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 8 * st);
+  }
+
+  // Tile kt, held in buffer buf (kt % 2); the DMA of tile kt+1 goes to the other.
+  auto tile_step = [&](int kt, auto buf) {
+    const uint16_t* const Kb = buf.value ? K1 : K0;
+    const uint16_t* const Vb = buf.value ? V1 : V0;
+    if (kt + 1 < n_tiles) issue_tile(kt + 1, std::integral_constant<int, 1 - buf.value>{});
     const int key0 = kt * kBN;
     const bool active = wave_has_rows && (!a.causal || key0 <= wt_hi);
     if (active) {
       // S^T[key][row] for the 64 keys of this tile, two 32-key blocks. The 8
       // A-operand fragments of a block are read from LDS before its MFMAs.
       f32x16 s[kBN / 32];
-      const uint16_t* kl = Ks + buf * L::kElems;
+      const uint16_t* kl = Kb;
 #pragma unroll
       for (int kb = 0; kb < kBN / 32; ++kb) {
         const uint16_t* krow = kl + (kb * 32 + l32) * L::kPitch + hq * (D / 2);
@@ -308,7 +376,7 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(KArgs a) {
 
       // O^T += V^T P^T. Element j of step u is key 16u + 8(j/4) + 4hq + j%4,
       // which the two transposing reads fetch for d = 32db + l%32.
-      const uint16_t* vl = Vs + buf * L::vElems;
+      const uint16_t* vl = Vb;
 #pragma unroll
       for (int u = 0; u < kBN / 16; ++u) {
         const uint16_t* p0 = vl + (16 * u + tr_row) * L::vPitch + tr_col;
@@ -320,42 +388,76 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(KArgs a) {
         for (int db = 0; db < D / 32; ++db) o[db] = mfma32x32x16(vfr[db], pf[u], o[db]);
       }
     }
-    if (kt + 1 < n_tiles) store_tile(buf ^ 1);
     __syncthreads();
+  };
+  for (int kt = 0; kt < n_tiles; kt += 2) {
+    tile_step(kt, B0{});
+    if (kt + 1 < n_tiles) tile_step(kt + 1, B1{});
   }
 
+  // Output: each pass stages D*2 bytes of each of the wave's 32 rows in QOw
+  // (all of a bf16 row, half of an fp32 row), then stores them row by row, 16
+  // bytes per lane.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (row_valid) {
-    const float inv = gate / l_tot;
-    const int oslot = a.out_slots ? gam * a.R + slot : head;
-    void* const outp = shared ? a.out_sh : a.out;
-    const size_t obase = shared ? ((size_t)b * a.T + t_row) * D + 4 * hq
-                                : b * a.o_b + oslot * a.o_h + t_row * a.o_t + 4 * hq;
+  const float inv = __int_as_float(tab[l32].w) / l_tot;
+  constexpr int kRowB = L::kPitch * 2;      // staged row pitch, bytes
+  constexpr int kG = D * 2 / 16;            // 16-byte granules per staged row
+  constexpr int kRowsPer = 64 / kG;         // rows per store instruction
+  char* const stage = reinterpret_cast<char*>(QOw);
+  const int n_pass = a.out_bf16 ? 1 : 2;
+  for (int pass = 0; pass < n_pass; ++pass) {
+    // o[db][4*i4 + j] holds d = 32db + 8i4 + 4hq + j of this lane's row.
+    if (a.out_bf16) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const size_t off = obase + 32 * db + 8 * i4;
-        const float x0 = o[db][4 * i4 + 0] * inv, x1 = o[db][4 * i4 + 1] * inv;
-        const float x2 = o[db][4 * i4 + 2] * inv, x3 = o[db][4 * i4 + 3] * inv;
-        if (a.out_bf16) {
-          uint2 w = {pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(outp) + off) = w;
-        } else {
-          *reinterpret_cast<float4*>(static_cast<float*>(outp) + off) = make_float4(x0, x1, x2, x3);
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = 32 * db + 8 * i4 + 4 * hq;
+          uint2 w = {pack_bf16x2(o[db][4 * i4] * inv, o[db][4 * i4 + 1] * inv),
+                     pack_bf16x2(o[db][4 * i4 + 2] * inv, o[db][4 * i4 + 3] * inv)};
+          *reinterpret_cast<uint2*>(stage + l32 * kRowB + d0 * 2) = w;
+        }
+    } else {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        if (db / (D / 64) != pass) continue;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = 32 * db + 8 * i4 + 4 * hq - pass * (D / 2);
+          *reinterpret_cast<float4*>(stage + l32 * kRowB + d0 * 4) =
+              make_float4(o[db][4 * i4] * inv, o[db][4 * i4 + 1] * inv, o[db][4 * i4 + 2] * inv,
+                          o[db][4 * i4 + 3] * inv);
         }
       }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 32 / kRowsPer; ++i) {
+      const int row = i * kRowsPer + lane / kG;
+      const int gran = lane % kG;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * kRowB + gran * 16);
+      const int rr = wrow0 + row;
+      if (rr < n_rows) {
+        const int4 ri = tab[row];
+        const int oslot = a.out_slots ? gam * a.R + ri.z : ri.y;
+        const size_t orow = shared ? ((size_t)b * a.T + ri.x) * D : b * a.o_b + oslot * a.o_h + ri.x * a.o_t;
+        char* const outp = static_cast<char*>(shared ? a.out_sh : a.out);
+        const size_t ob = orow * (a.out_bf16 ? 2 : 4) + (size_t)pass * D * 2 + gran * 16;
+        *reinterpret_cast<u32x4*>(outp + ob) = v;
+      }
+    }
+    if (pass + 1 < n_pass) __syncthreads();
   }
 }
 
-template <int D, int W, int BN>
+template <int D, int W, int BN, int OCC>
 hipError_t launch_dw(KArgs a, const AttnParams& p, hipStream_t stream) {
   a.n_row_tiles = div_up(p.T * p.R, W * 32);
   const dim3 grid(a.n_row_tiles * a.BG), block(W * 64);
   if (p.idx)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, W, BN, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, W, BN, OCC, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, W, BN, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, W, BN, OCC, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -397,8 +499,8 @@ hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     n_cu = 256;
   const long long large_grid = (long long)a.BG * div_up(p.T * p.R, kWavesLarge * 32);
-  if (large_grid >= 2ll * n_cu) return launch_dw<D, kWavesLarge, kBNLarge>(a, p, stream);
-  return launch_dw<D, kWavesSmall, kBNSmall>(a, p, stream);
+  if (large_grid * kWavesLarge >= 24ll * n_cu) return launch_dw<D, kWavesLarge, kBNLarge, kOccLarge>(a, p, stream);
+  return launch_dw<D, kWavesSmall, kBNSmall, kOccSmall>(a, p, stream);
 }
 
 }  // namespace
