@@ -372,7 +372,7 @@ def main():
     if "prefill" in res:
         p = res["prefill"]
         line["roofline"] = {
-            "kernel": "attn_bf16_kernel<128,12,32,false>",
+            "kernel": "attn_bf16_kernel<128,12,32,3,false>",
             "bound": "mfma",
             "achieved": p["tflops"],
             "peak": PEAK_BF16_TFLOPS,
