@@ -92,6 +92,34 @@ def test_gqe_headline_shape(top_k):
     assert worst <= TOL_BF16, worst
 
 
+def test_gqe_large_grid_ragged():
+    """B=16, h=32, g=8, T=2000, k=2: the routed rows fill the large-grid
+    configuration (1408 workgroups of 384 rows) and the last 32-key tile is
+    partial. Indices bit-exact, zero rows exactly where heads were dropped, and
+    sampled kept rows (the last tokens among them) equal gate x the oracle's row."""
+    B, h, g, T, d, top_k = 16, 32, 8, 2000, 128, 2
+    dv = dev()
+    say(f"gqe large grid B={B} h={h} g={g} T={T} k={top_k}")
+    q, k, v, lg = gqe_inputs(B, h, g, T, d, "bf16", seed=77, device=dv)
+    out, idx, gate = _run(q, k, v, lg, top_k, out_dtype=torch.bfloat16)
+    ridx, rgate = oracle.gqe_topk_ref(lg.cpu(), g, top_k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert max_abs(gate, rgate) <= TOL_GATE
+    kept = torch.zeros(B, T, h, dtype=torch.bool, device=dv)
+    kept.scatter_(2, idx.view(B, T, -1).long(), True)
+    assert torch.equal((out != 0).any(-1).permute(0, 2, 1), kept)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    worst = 0.0
+    for t in sample_tokens(T, 12, seed=78, tile=32):
+        for bb in (0, B - 1):
+            for gam in (0, 3, g - 1):
+                for j in range(top_k):
+                    i = int(ridx[bb, t, gam, j])
+                    ref = rgate[bb, t, gam, j] * oracle.gqa_ref_row(qc, kc, vc, bb, i, t)
+                    worst = max(worst, float(np.abs(np64(out[bb, i, t]) - ref).max()))
+    assert worst <= TOL_BF16, worst
+
+
 @pytest.mark.parametrize("B,h,g,T,d,ks,seed", gqe_sweep_points(),
                          ids=lambda x: str(x) if not isinstance(x, tuple) else "k" + "".join(map(str, x)))
 def test_gqe_sweep_point(B, h, g, T, d, ks, seed):

@@ -97,6 +97,38 @@ def test_bf16_headline_shape_sampled_rows():
     assert worst <= TOL_BF16, worst
 
 
+def _large_grid(B, h, g, T):
+    """True when the launch takes the 12-wave, 32-key-tile configuration (at
+    least 24 waves of 384-row work per CU)."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    return B * g * -(-(T * (h // g)) // 384) * 12 >= 24 * n_cu
+
+
+@pytest.mark.parametrize("T,d,causal,out_dt", [
+    (2000, 128, True, torch.bfloat16),   # the last key tile holds 16 keys
+    (2001, 128, True, torch.float32),    # one key in the last tile; fp32 out (two staging passes)
+    (1999, 64, False, torch.bfloat16),   # d = 64, no causal mask, only the tail
+])
+def test_bf16_large_grid_ragged(T, d, causal, out_dt):
+    """B=8, h=32, g=8: enough row tiles for the large-grid configuration, with T
+    not a multiple of its 32-key tile, so the last K/V tile is partial (its keys
+    past T are clamped when staged and masked). The last tokens and sampled
+    rows elsewhere, against the oracle."""
+    B, h, g = 8, 32, 8
+    assert _large_grid(B, h, g, T)
+    say(f"bf16 large grid B={B} h={h} g={g} T={T} d={d} causal={causal} out={out_dt}")
+    q, k, v = prefill_inputs(B, h, g, T, d, "bf16", seed=300 + T + d, device=dev())
+    out = _run(q, k, v, causal=causal, out_dtype=out_dt)
+    qc, kc, vc, oc = q.cpu(), k.cpu(), v.cpu(), out.cpu()
+    worst = 0.0
+    for t in sample_tokens(T, 24, seed=T, tile=32):
+        for b in (0, B - 1):
+            for i in (0, 13, h - 1):
+                ref = oracle.gqa_ref_row(qc, kc, vc, b, i, t, causal=causal)
+                worst = max(worst, float(np.abs(np64(oc[b, i, t]) - ref).max()))
+    assert worst <= TOL_BF16, worst
+
+
 def test_bf16_headline_shape_unit_values():
     """At the headline shape with V = 1 everywhere every output is 1 (the
     weights of a row sum to one), whatever q and k are."""
