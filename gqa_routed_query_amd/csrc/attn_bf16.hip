@@ -35,10 +35,18 @@
 //  * Q comes in and the output goes out through a per-wave LDS region, so
 //    both move whole rows per instruction; read straight from HBM in the
 //    fragment layouts, each instruction would touch 16 bytes of 32 rows.
-//  * Causal grids are issued heaviest-first; (batch, group) is the fastest
-//    varying part of the block index, so with B*g a multiple of 8 all tiles of
-//    one group land on one XCD and share its L2.
+//  * (batch, group) is the fastest varying part of the block index, so with B*g
+//    a multiple of 8 all tiles of one group land on one XCD and share its L2.
+//    The row tiles of a causal grid differ in cost (the number of visible key
+//    tiles), and their dispatch order is planned on the host (plan_order).
+#include <algorithm>
+#include <functional>
+#include <map>
+#include <mutex>
+#include <queue>
+#include <tuple>
 #include <type_traits>
+#include <vector>
 
 #include "common.h"
 #include "launch.h"
@@ -53,6 +61,7 @@ namespace {
 constexpr int kWavesLarge = 12, kBNLarge = 32, kOccLarge = 3;
 constexpr int kWavesSmall = 8, kBNSmall = 64, kOccSmall = 2;
 constexpr float kRescale = 8.0f;                      // lazy-rescale threshold, log2 units
+constexpr int kMaxOrder = 48;                         // row-tile bands with a planned dispatch order
 
 template <int D, int W, int kBN>
 struct Tile {
@@ -96,6 +105,10 @@ struct KArgs {
   const uint16_t* q_sh;
   void* out_sh;
   int sh_kv;
+  // Causal grids: block band i (blocks i*BG .. i*BG + BG-1, one per problem)
+  // runs row tile order[i] when n_order > 0, else row tile n_row_tiles-1-i.
+  int n_order;
+  uint16_t order[kMaxOrder];
 };
 
 // Zero the output rows of heads the router did not keep, for the tokens whose
@@ -152,7 +165,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
 
   const int bid = blockIdx.x;
   const int bg = bid % a.BG;
-  const int tile = a.causal ? (a.n_row_tiles - 1 - bid / a.BG) : (bid / a.BG);
+  const int band = bid / a.BG;
+  const int tile = !a.causal ? band : a.n_order ? (int)a.order[band] : a.n_row_tiles - 1 - band;
   // The shared head's problem (uniform per block; only routed launches carry one).
   const bool shared = ROUTED && bg >= a.BG_main;
   const int b = shared ? bg - a.BG_main : bg / a.g;
@@ -450,9 +464,97 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   }
 }
 
+// Dispatch order of the row-tile bands of a causal grid. The hardware hands
+// blocks to CUs in index order as CUs free up; a band is one row tile of every
+// problem. Heaviest first leaves the last round short of work: at B=4, h=32,
+// g=8, T=2048 two rounds end together and 192 light jobs remain for 256 CUs.
+// The order is searched on a model of that dispatch: a job costs its key tiles
+// plus a fixed cost, goes to the CU that frees first, and pairwise swaps of
+// bands are kept while they shorten the simulated end. The per-job fixed cost
+// (prologue and epilogue) was fitted by measurement: about 4 tiles of 32 keys.
+// Cached per shape; shapes with more bands keep heaviest first.
+struct OrderShape {
+  int n_bands, rows, R, T, kBN, BG_main, B_sh, n_cu;
+  bool operator<(const OrderShape& o) const {
+    return std::tie(n_bands, rows, R, T, kBN, BG_main, B_sh, n_cu) <
+           std::tie(o.n_bands, o.rows, o.R, o.T, o.kBN, o.BG_main, o.B_sh, o.n_cu);
+  }
+};
+
+double simulate_dispatch(const std::vector<int>& order, const std::vector<double>& cost_main,
+                         const std::vector<double>& cost_sh, int per_main, int per_sh, int n_cu) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  for (int i = 0; i < n_cu; ++i) free_at.push(0.0);
+  double end = 0.0;
+  for (int band : order)
+    for (int j = 0; j < per_main + per_sh; ++j) {
+      const double t = free_at.top() + (j < per_main ? cost_main[band] : cost_sh[band]);
+      free_at.pop();
+      free_at.push(t);
+      end = std::max(end, t);
+    }
+  return end;
+}
+
+std::vector<uint16_t> plan_order(const OrderShape& s) {
+  // Key tiles of row tile i of a problem with n_rows = T*R rows, R per token.
+  auto cost = [&](int i, int R, double fixed) {
+    const int n_rows = s.T * R, row0 = i * s.rows;
+    if (row0 >= n_rows) return 0.0;
+    const int t_last = (std::min(row0 + s.rows, n_rows) - 1) / R;
+    return (double)div_up(t_last + 1, s.kBN) + fixed;
+  };
+  const double fixed = 128.0 / s.kBN;  // ≈ 4 tiles of 32 keys
+  std::vector<double> cost_main(s.n_bands), cost_sh(s.n_bands);
+  for (int i = 0; i < s.n_bands; ++i) {
+    cost_main[i] = cost(i, s.R, fixed);
+    cost_sh[i] = cost(i, 1, fixed);
+  }
+  // With whole problems per XCD slice (blocks go to XCDs round-robin), one
+  // eighth of the CUs and of each band is an exact model.
+  int per_main = s.BG_main, per_sh = s.B_sh, n_cu = s.n_cu;
+  if (per_main % 8 == 0 && per_sh % 8 == 0 && n_cu % 8 == 0) {
+    per_main /= 8;
+    per_sh /= 8;
+    n_cu /= 8;
+  }
+  std::vector<int> order(s.n_bands);
+  for (int i = 0; i < s.n_bands; ++i) order[i] = s.n_bands - 1 - i;  // heaviest first
+  double best = simulate_dispatch(order, cost_main, cost_sh, per_main, per_sh, n_cu);
+  for (int pass = 0; pass < 4; ++pass) {
+    bool improved = false;
+    for (int i = 0; i < s.n_bands; ++i)
+      for (int j = i + 1; j < s.n_bands; ++j) {
+        std::swap(order[i], order[j]);
+        const double m = simulate_dispatch(order, cost_main, cost_sh, per_main, per_sh, n_cu);
+        if (m < best - 1e-9) {
+          best = m;
+          improved = true;
+        } else {
+          std::swap(order[i], order[j]);
+        }
+      }
+    if (!improved) break;
+  }
+  return std::vector<uint16_t>(order.begin(), order.end());
+}
+
+void set_order(KArgs& a, const OrderShape& s) {
+  a.n_order = 0;
+  if (!a.causal || s.n_bands < 2 || s.n_bands > kMaxOrder) return;
+  static std::mutex mu;
+  static std::map<OrderShape, std::vector<uint16_t>> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(s);
+  if (it == cache.end()) it = cache.emplace(s, plan_order(s)).first;
+  std::copy(it->second.begin(), it->second.end(), a.order);
+  a.n_order = s.n_bands;
+}
+
 template <int D, int W, int BN, int OCC>
-hipError_t launch_dw(KArgs a, const AttnParams& p, hipStream_t stream) {
+hipError_t launch_dw(KArgs a, const AttnParams& p, hipStream_t stream, int n_cu) {
   a.n_row_tiles = div_up(p.T * p.R, W * 32);
+  set_order(a, OrderShape{a.n_row_tiles, W * 32, p.R, p.T, BN, a.BG_main, a.BG - a.BG_main, n_cu});
   const dim3 grid(a.n_row_tiles * a.BG), block(W * 64);
   if (p.idx)
     hipLaunchKernelGGL((attn_bf16_kernel<D, W, BN, OCC, true>), grid, block, 0, stream, a);
@@ -499,8 +601,9 @@ hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
       hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     n_cu = 256;
   const long long large_grid = (long long)a.BG * div_up(p.T * p.R, kWavesLarge * 32);
-  if (large_grid * kWavesLarge >= 24ll * n_cu) return launch_dw<D, kWavesLarge, kBNLarge, kOccLarge>(a, p, stream);
-  return launch_dw<D, kWavesSmall, kBNSmall, kOccSmall>(a, p, stream);
+  if (large_grid * kWavesLarge >= 24ll * n_cu)
+    return launch_dw<D, kWavesLarge, kBNLarge, kOccLarge>(a, p, stream, n_cu);
+  return launch_dw<D, kWavesSmall, kBNSmall, kOccSmall>(a, p, stream, n_cu);
 }
 
 }  // namespace
