@@ -12,17 +12,19 @@
 // router_proj_kernel: logits = x W_r^T for a tile of 32 tokens, then the same
 // selection. The contraction is skinny (h <= 64 outputs per token over d_model
 // inputs) and HBM-bound on x, so it runs on v_mfma_f32_32x32x16_bf16 with the
-// heads as the 32 A rows and the tokens as the 32 B columns. x is staged
-// through LDS in 1024-column chunks (2 KiB of each of the 32 token rows), each
-// wave instruction loading 1 KiB of one row, double-buffered in registers;
-// workgroups start at different chunks so that the whole chip does not read
-// the same column window (rows d_model apart) at once. The 8 waves split each
-// chunk's columns for the MFMAs, read W_r from L2 (256 KiB at h=32,
-// d_model=4096) one chunk ahead, and reduce through LDS. The selection then
-// reads the summed logits from LDS, one thread per (token, group).
+// heads as the 32 A rows and the tokens as the 32 B columns. x and W_r move
+// to LDS by DMA (global_load_lds_dwordx4) in 256-column chunks, with three
+// chunks in flight behind the one in use (two for h > 32), no registers
+// staging them. Workgroups start at different chunks, so that the whole chip
+// does not read the same column window (rows d_model apart) at once. The 8
+// waves split each chunk's columns for the MFMAs and reduce through LDS. The
+// selection then reads the summed logits from LDS, one thread per (token,
+// group).
 #include "common.h"
 #include "launch.h"
 #include "topk.h"
+
+#include <type_traits>
 
 namespace gqa {
 namespace {
@@ -41,8 +43,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(RouterParams p) {
 
 constexpr int kPW = 8;      // waves per workgroup
 constexpr int kPTok = 32;   // tokens per workgroup
-constexpr int kKC = 1024;   // d_model columns per LDS chunk (2 KiB of a bf16 row)
-constexpr int kXPitch = kKC + 8;  // 16-byte pad: B-operand reads of 16 rows hit distinct banks
+constexpr int kKC = 256;    // d_model columns per chunk (512 bytes of a bf16 row)
+constexpr int kRowEl = kKC;               // LDS row pitch in elements: 512 B, XOR-swizzled granules
+constexpr int kTileEl = 32 * kRowEl;      // one 32-row tile (x rows or a block of 32 W_r rows)
+constexpr int kSteps = kKC / kPW / 16;    // 16-wide MFMA k-steps per wave and chunk (2)
 
 struct ProjArgs {
   const uint16_t* x;  // [n_tok, dm] bf16
@@ -53,137 +57,156 @@ struct ProjArgs {
   int n_tok, dm, h, g, k;
 };
 
+// LDS granule (16 bytes) of row r, logical granule q of a 512-byte row: the
+// granule index is XORed with r mod 8, so the 16-byte reads of one granule
+// column by rows 0..7 (one MFMA operand step) fall in eight different banks.
+__device__ __forceinline__ int swz(int r, int q) { return r * (kRowEl / 8) + (q ^ (r & 7)); }
+
+// Byte address of an LDS location, for ds_read operands.
+__device__ __forceinline__ unsigned lds_addr(const uint16_t* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
+}
+
 template <int HB>  // head blocks of 32 (h <= 32 * HB)
 __global__ __launch_bounds__(kPW * 64) void router_proj_kernel(ProjArgs a) {
-  constexpr int kPitch = kPTok + 1;
-  constexpr int kXElems = kPTok * kXPitch;
-  constexpr int kRedFloats = kPW * HB * 32 * kPitch;
-  constexpr int kSmem = (2 * kXElems * 2 > kRedFloats * 4) ? 2 * kXElems * 2 : kRedFloats * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmem];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // two chunk buffers [kPTok][kXPitch]
-  float* red = reinterpret_cast<float*>(smem);       // reused after the last chunk
+  // Buffers: the chunk in use and NB-1 in flight. Each holds the chunk's 32
+  // token rows and its HB blocks of 32 W_r rows. One array per buffer, so that
+  // with the buffer fixed at compile time the compiler can tell the DMA into
+  // one buffer from the reads of another.
+  constexpr int NB = HB == 1 ? 4 : 3;
+  constexpr int kBufEl = (1 + HB) * kTileEl;
+  __shared__ __attribute__((aligned(16))) uint16_t B0[kBufEl], B1[kBufEl], B2[kBufEl];
+  __shared__ __attribute__((aligned(16))) uint16_t B3[NB == 4 ? kBufEl : 8];
+  constexpr int kDmaPerWave = (1 + HB) * 16 / kPW;  // 1 KiB DMA instructions (two rows each) per wave and chunk
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hq = lane >> 5;
   const int tok0 = blockIdx.x * kPTok;
-
-  // Chunk loads: wave w fetches rows 4w .. 4w+3 of the tile, one instruction
-  // per row, lane l taking the row's 16-byte piece l (1 KiB contiguous).
-  constexpr int kRowsPerWave = kPTok / kPW;
-  constexpr int kPieces = kKC / 512;
-  u32x4 xr[kRowsPerWave * kPieces];
-  auto load_chunk = [&](int c0, int width) {
-#pragma unroll
-    for (int j = 0; j < kRowsPerWave; ++j)
-#pragma unroll
-      for (int q = 0; q < kPieces; ++q) {
-        const int t = tok0 + wave * kRowsPerWave + j;
-        const int col = q * 512 + lane * 8;
-        const bool ok = t < a.n_tok && col < width;
-        xr[j * kPieces + q] = ok ? *reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.dm + c0 + col)
-                                 : u32x4{0u, 0u, 0u, 0u};
-      }
-  };
-  auto store_chunk = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < kRowsPerWave; ++j)
-#pragma unroll
-      for (int q = 0; q < kPieces; ++q)
-        *reinterpret_cast<u32x4*>(xs + buf * kXElems + (wave * kRowsPerWave + j) * kXPitch + q * 512 + lane * 8) =
-            xr[j * kPieces + q];
+  const int n_chunks = div_up(a.dm, kKC);
+  // Workgroups start at different chunks, so that the chip does not read the
+  // same column window of every row at once.
+  const int c_first = blockIdx.x % n_chunks;
+  auto chunk_col = [&](int c) { return ((c + c_first) % n_chunks) * kKC; };
+  auto buf = [&](auto nb) -> uint16_t* {
+    return nb.value == 0 ? B0 : nb.value == 1 ? B1 : nb.value == 2 ? B2 : B3;
   };
 
-  bool w_ok[HB];
-  const uint16_t* wr[HB];
+  // Chunk c into buffer nb by DMA. Instruction i of the chunk moves rows
+  // 2i, 2i+1 of the chunk's (1 + HB) 32-row tiles (token rows, then W_r rows):
+  // lane l moves granule l % 32 of row 2i + l / 32, written at its swizzled
+  // place, i.e. loaded from the granule that belongs there. Rows past n_tok or
+  // h and columns past the row end load valid memory that is never used, so
+  // every chunk costs kDmaPerWave instructions per wave, which `step` counts on.
+  auto issue = [&](int c, auto nb) {
+    uint16_t* const Xb = buf(nb);
+    const int c0 = chunk_col(c);
+    const int width = min(kKC, a.dm - c0);
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int head = hb * 32 + l32;
-    w_ok[hb] = head < a.h;
-    wr[hb] = a.w + (size_t)(w_ok[hb] ? head : 0) * a.dm + 8 * hq;
-  }
+    for (int j = 0; j < kDmaPerWave; ++j) {
+      const int i = wave * kDmaPerWave + j;  // 0 .. (1+HB)*16-1, uniform
+      const int tl = i / 16;                 // tile: 0 = tokens, 1.. = W_r head blocks
+      const int r = 2 * (i % 16) + lane / 32;
+      const int q = (lane & 31) ^ (r & 7);   // logical granule stored at physical granule lane % 32
+      const int col = q * 8 < width ? q * 8 : 0;
+      const uint16_t* src = tl == 0 ? a.x + (size_t)min(tok0 + r, a.n_tok - 1) * a.dm
+                                    : a.w + (size_t)min((tl - 1) * 32 + r, a.h - 1) * a.dm;
+      __builtin_amdgcn_global_load_lds(src + c0 + col,
+                                       (__attribute__((address_space(3))) void*)(Xb + tl * kTileEl + (i % 16) * 2 * kRowEl),
+                                       16, 0, 0);
+    }
+  };
+
   f32x16 acc[HB];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x16{};
+  using N0 = std::integral_constant<int, 0>;
+  using N1 = std::integral_constant<int, 1>;
+  using N2 = std::integral_constant<int, 2>;
+  using N3 = std::integral_constant<int, 3>;
+  issue(0, N0{});
+  if (n_chunks > 1) issue(1, N1{});
+  if (NB == 4 && n_chunks > 2) issue(2, N2{});
 
-  // A chunk's columns are split over the waves: wave w takes
-  // [w * width/8, (w+1) * width/8), at most kSteps 16-wide MFMA steps (lane
-  // half hq holds 8 of each step's 16). W_r fragments of the next chunk are
-  // fetched from L2 together with its x rows.
-  constexpr int kSteps = kKC / kPW / 16;
-  bf16x8 wn[HB][kSteps];
-  auto load_w = [&](int c0, int width) {
-    const int per = width / kPW;
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st)
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb)
-        wn[hb][st] = (16 * st < per && w_ok[hb])
-                         ? *reinterpret_cast<const bf16x8*>(wr[hb] + c0 + wave * per + 16 * st)
-                         : bf16x8{};
-  };
-
-  const int n_chunks = div_up(a.dm, kKC);
-  const int c_first = blockIdx.x % n_chunks;
-  auto chunk_col = [&](int c) { return ((c + c_first) % n_chunks) * kKC; };
-  load_chunk(chunk_col(0), min(kKC, a.dm - chunk_col(0)));
-  load_w(chunk_col(0), min(kKC, a.dm - chunk_col(0)));
-  store_chunk(0);
-  __syncthreads();
-  for (int c = 0; c < n_chunks; ++c) {
-    const int c0 = chunk_col(c);
-    const int per = min(kKC, a.dm - c0) / kPW;  // a multiple of 16
-    bf16x8 wc[HB][kSteps];
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st)
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) wc[hb][st] = wn[hb][st];
-    if (c + 1 < n_chunks) {
-      const int n0 = chunk_col(c + 1);
-      load_chunk(n0, min(kKC, a.dm - n0));
-      load_w(n0, min(kKC, a.dm - n0));
+  // Chunk c in buffer nb. Before the barrier each wave waits for its own DMA
+  // of chunk c; the NB-2 chunks issued after it stay in flight.
+  constexpr int kAhead = (NB - 2) * kDmaPerWave;
+  auto step = [&](int c, auto nb) {
+    if (c + NB - 2 < n_chunks) {
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kAhead) : "memory");
+    } else if (NB == 4 && c + 1 < n_chunks) {
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kDmaPerWave) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    const uint16_t* xb_row = xs + (c & 1) * kXElems + l32 * kXPitch + wave * per + 8 * hq;
+    // The buffer NB-1 steps ahead held chunk c-1, which every wave has finished.
+    if (c + NB - 1 < n_chunks) issue(c + NB - 1, std::integral_constant<int, (nb.value + NB - 1) % NB>{});
+    const uint16_t* const Xb = buf(nb);
+    const int per = min(kKC, a.dm - chunk_col(c)) / kPW;  // a multiple of 16
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       if (16 * st >= per) break;
-      const bf16x8 xb = *reinterpret_cast<const bf16x8*>(xb_row + 16 * st);
+      const int q = (wave * per + 16 * st + 8 * hq) / 8;  // logical granule of this step
+      const unsigned ax = lds_addr(Xb + swz(l32, q) * 8);
+      // The step's operand reads, written out with their own wait: the
+      // compiler's tracking of the DMAs into the other buffers would otherwise
+      // put a full vmcnt(0) wait before the first read after the loop's back
+      // edge, draining the chunks in flight.
+      bf16x8 xb, wa[HB];
+      if (HB == 1) {
+        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:%3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=v"(xb), "=v"(wa[0])
+                     : "v"(ax), "n"(kTileEl * 2));
+      } else {
+        asm volatile(
+            "ds_read_b128 %0, %3\n\tds_read_b128 %1, %3 offset:%4\n\tds_read_b128 %2, %3 offset:%5\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=v"(xb), "=v"(wa[0]), "=v"(wa[HB - 1])
+            : "v"(ax), "n"(kTileEl * 2), "n"(kTileEl * 4));
+      }
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32x32x16(wc[hb][st], xb, acc[hb]);
+      for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32x32x16(wa[hb], xb, acc[hb]);
     }
-    if (c + 1 < n_chunks) store_chunk((c + 1) & 1);
-    __syncthreads();
+  };
+  for (int c = 0; c < n_chunks; c += NB) {
+    step(c, N0{});
+    if (c + 1 < n_chunks) step(c + 1, N1{});
+    if (c + 2 < n_chunks) step(c + 2, N2{});
+    if (NB == 4 && c + 3 < n_chunks) step(c + 3, N3{});
   }
-
-  // acc[hb][i] = partial logit of head hb*32 + 8(i/4) + 4hq + i%4, token l%32
-  // (the LDS chunks are no longer read: the last barrier above).
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int head = hb * 32 + 8 * (i >> 2) + 4 * hq + (i & 3);
-      red[(wave * HB * 32 + head) * kPitch + l32] = acc[hb][i];
-    }
   __syncthreads();
 
+  // acc[hb][i] = partial logit of head hb*32 + 8(i/4) + 4hq + i%4, token l%32.
+  // Reduce over the waves through LDS, one block of 32 heads at a time.
+  constexpr int kPitch = kPTok;  // writes and reads both run along consecutive tokens
+  static_assert(kPW * 32 * kPitch * 4 <= kBufEl * 2, "a reduction round fits in one buffer");
+  float* const red = reinterpret_cast<float*>(B0);
+  float* const lg = reinterpret_cast<float*>(B1);  // summed logits [HB*32][kPitch]
   const int r = a.h / a.g;
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[(wave * 32 + 8 * (i >> 2) + 4 * hq + (i & 3)) * kPitch + l32] = acc[hb][i];
+    __syncthreads();
+    for (int item = tid; item < 32 * kPTok; item += kPW * 64) {
+      const int hh = item / kPTok, t = item % kPTok;
+      float v = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < kPW; ++wv) v += red[(wv * 32 + hh) * kPitch + t];
+      const int head = hb * 32 + hh;
+      lg[head * kPitch + t] = v;
+      if (a.logits && head < a.h && tok0 + t < a.n_tok) a.logits[(size_t)(tok0 + t) * a.h + head] = v;
+    }
+    __syncthreads();
+  }
   for (int item = tid; item < kPTok * a.g; item += kPW * 64) {
     const int t = item % kPTok;
     const int gam = item / kPTok;
     if (tok0 + t >= a.n_tok) continue;
     const size_t row = (size_t)(tok0 + t);
-    // Sum the waves' partials in place (this item owns column t of its heads).
-    for (int e = 0; e < r; ++e) {
-      const int head = gam * r + e;
-      float v = 0.0f;
-#pragma unroll
-      for (int wv = 0; wv < kPW; ++wv) v += red[(wv * HB * 32 + head) * kPitch + t];
-      red[head * kPitch + t] = v;
-      if (a.logits) a.logits[row * a.h + head] = v;
-    }
-    topk_select([&](int e) { return red[(gam * r + e) * kPitch + t]; }, r, a.k, gam * r,
+    topk_select([&](int e) { return lg[(gam * r + e) * kPitch + t]; }, r, a.k, gam * r,
                 a.idx + (row * a.g + gam) * a.k, a.gate + (row * a.g + gam) * a.k);
   }
 }
