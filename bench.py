@@ -153,6 +153,10 @@ def main():
     if run_gqe:
         gq_, gk, gv, glg = gqe_inputs(wg.B, wg.h, wg.g, wg.T, wg.d, "bf16", seed=wg.seed, device=dev)
         gout = torch.empty_like(gq_)
+        gws = {}
+        for kk in wg.top_k:
+            nb = gq.gqe_workspace_bytes(wg.B, wg.h, wg.g, wg.T, wg.d, kk)
+            gws[kk] = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
         dense_gqe_flops = 2.0 * wg.B * wg.h * wg.d * wg.T * (wg.T + 1)
     torch.cuda.synchronize()
 
@@ -171,7 +175,8 @@ def main():
         if run_gqe:
             for kk in wg.top_k:
                 with (t_gqe[kk] if timed else Timer(torch)):
-                    gq.gqe_routed_prefill(gq_, gk, gv, glg, kk, causal=True, out=gout)
+                    gq.gqe_routed_prefill(gq_, gk, gv, glg, kk, causal=True, out=gout,
+                                          workspace=gws[kk])
             with (t_gqa_same if timed else Timer(torch)):
                 gq.gqa_prefill(gq_, gk, gv, causal=True, out=gout)
 
@@ -302,7 +307,7 @@ def main():
     if run_gqe and not args.no_sweep:
         if run_prefill:
             del pout
-        del gq_, gk, gv, glg, gout
+        del gq_, gk, gv, glg, gout, gws
         torch.cuda.empty_cache()
         for (B, h, g, T, d, ks, seed) in gqe_sweep_points():
             q, k, v, lg = gqe_inputs(B, h, g, T, d, "bf16", seed=seed, device=dev)
@@ -333,7 +338,10 @@ def main():
                     f"speed-up {dense_ms/ms:.2f}")
                 del qs
             for kk in ks:
-                ms = timed(lambda: gq.gqe_routed_prefill(q, k, v, lg, kk, causal=True, out=out))
+                wsb = gq.gqe_workspace_bytes(B, h, g, T, d, kk)
+                ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+                ms = timed(lambda: gq.gqe_routed_prefill(q, k, v, lg, kk, causal=True, out=out,
+                                                         workspace=ws))
                 fl = dense_flops * kk / (h // g)
                 gsweep.append(dict(B=B, h=h, g=g, T=T, d=d, top_k=kk, routed_us=ms * 1e3,
                                    dense_us=dense_ms * 1e3, speedup=dense_ms / ms,

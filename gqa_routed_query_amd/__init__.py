@@ -30,6 +30,7 @@ from ._binding import (  # noqa: F401
     gqe_routed_decode,
     gqe_routed_prefill,
     gqe_router,
+    gqe_workspace_bytes,
     last_error,
     lib_path,
     status_string,

@@ -49,7 +49,9 @@ def _load():
                                vp, sz, vp]
     lib.gqe_routed_prefill.restype = i32
     lib.gqe_routed_prefill.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32,
-                                       i32, i32, i32, f32, i32, vp]
+                                       i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.gqe_workspace_bytes.restype = sz
+    lib.gqe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.gqe_routed_decode.restype = i32
     lib.gqe_routed_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32,
                                       i32, i32, i32, f32, vp, sz, vp]
@@ -178,9 +180,17 @@ def gqa_decode(q, k_cache, v_cache, lens, scale: float | None = None, out=None,
     return out
 
 
+def gqe_workspace_bytes(B: int, h: int, g: int, T: int, d: int, top_k: int) -> int:
+    """Bytes of workspace gqe_routed_prefill can use at this shape (0: none)."""
+    return int(_lib.gqe_workspace_bytes(B, h, g, T, d, top_k))
+
+
 def gqe_routed_prefill(q, k, v, router_logits, top_k: int, causal: bool = True,
-                       scale: float | None = None, out=None, out_dtype=None):
-    """GQE routed prefill -> (out [B,h,T,d], idx [B,T,g,k] int32, gate [B,T,g,k] fp32)."""
+                       scale: float | None = None, out=None, out_dtype=None, workspace=True):
+    """GQE routed prefill -> (out [B,h,T,d], idx [B,T,g,k] int32, gate [B,T,g,k] fp32).
+
+    workspace: True (default) allocates the gqe_workspace_bytes(...) the call
+    can use, None or False passes none, or a uint8 device tensor to use."""
     dev = _dev(q, k, v, router_logits)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("expected q [B,h,T,d] and k, v [B,g,T,d]")
@@ -202,11 +212,20 @@ def gqe_routed_prefill(q, k, v, router_logits, top_k: int, causal: bool = True,
     idx = torch.empty((B, T, g, kk), dtype=torch.int32, device=dev)
     gate = torch.empty((B, T, g, kk), dtype=torch.float32, device=dev)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if workspace is True:
+        nbytes = gqe_workspace_bytes(B, h, g, T, d, int(top_k)) if 1 <= top_k <= h // max(g, 1) else 0
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+    elif workspace is False:
+        workspace = None
+    if workspace is not None:
+        _dev(q, workspace)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = _lib.gqe_routed_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                  router_logits.data_ptr(), int(top_k), out.data_ptr(),
                                  idx.data_ptr(), gate.data_ptr(), B, h, g, T, d,
                                  _dt(q, "q"), _dt(out, "out"), scale, int(bool(causal)),
-                                 _stream(dev))
+                                 ws_ptr, ws_bytes, _stream(dev))
     _check("gqe_routed_prefill", st)
     return out, idx, gate
 

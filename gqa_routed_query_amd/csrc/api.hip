@@ -125,7 +125,7 @@ gqa_status prepare_decode(const void* q, const void* k_cache, const void* v_cach
 
 extern "C" {
 
-int gqa_abi_version(void) { return 1; }
+int gqa_abi_version(void) { return 2; }
 
 const char* gqa_status_string(gqa_status s) {
   switch (s) {
@@ -281,10 +281,16 @@ gqa_status gqe_router(const void* x, const void* w_r, int top_k, float* logits, 
   return hip_status(gqa::launch_router_proj(p, static_cast<hipStream_t>(stream)), "gqe_router launch");
 }
 
+size_t gqe_workspace_bytes(int B, int h, int g, int T, int d, int top_k) {
+  if (B <= 0 || T <= 0 || h <= 0 || g <= 0 || h % g != 0 || top_k < 1 || top_k > h / g) return 0;
+  if (!gqa::attn_bf16_supports(d)) return 0;
+  return gqa::attn_bf16_split_ws_bytes(B, g, T, d, top_k, 1);
+}
+
 gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v, const float* router_logits,
                               int top_k, void* out, int32_t* topk_idx, float* topk_gate, int B, int h,
                               int g, int T, int d, gqa_dtype in_dtype, gqa_dtype out_dtype, float scale,
-                              int causal, void* stream) {
+                              int causal, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = '\0';
   gqa_status s = check_prefill_shape(q, k, v, out, B, h, g, T, d, in_dtype, out_dtype, scale, causal);
   if (s != GQA_OK) return s;
@@ -294,7 +300,13 @@ gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v, const
   if (B == 0 || T == 0) return GQA_OK;
   if (!router_logits || !topk_idx || !topk_gate)
     return fail(GQA_ERR_INVALID_ARG, "null router_logits, topk_idx or topk_gate pointer");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   if ((s = check_device()) != GQA_OK) return s;
+  // Key splitting (bf16 causal launches only) needs the workspace.
+  const size_t need = in_dtype == GQA_BF16 ? gqa::attn_bf16_split_ws_bytes(B, g, T, d, top_k, causal) : 0;
+  if (workspace && workspace_bytes < need)
+    return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   auto st = static_cast<hipStream_t>(stream);
   gqa::RouterParams rp{router_logits, topk_idx, topk_gate, B, T, h, g, top_k};
   if ((s = hip_status(gqa::launch_router(rp, st), "gqe router launch")) != GQA_OK) return s;
@@ -308,6 +320,7 @@ gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v, const
   p.causal = causal;
   p.out_bf16 = out_dtype == GQA_BF16;
   p.zero_unselected = 1;
+  p.split_ws = need > 0 ? workspace : nullptr;
   const hipError_t e = in_dtype == GQA_BF16 ? gqa::launch_attn_bf16(p, st) : gqa::launch_attn_f32(p, st);
   return hip_status(e, "gqe routed attention launch");
 }

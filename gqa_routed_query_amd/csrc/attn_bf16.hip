@@ -109,6 +109,14 @@ struct KArgs {
   // runs row tile order[i] when n_order > 0, else row tile n_row_tiles-1-i.
   int n_order;
   uint16_t order[kMaxOrder];
+  // Key-split slots (routed launches given a workspace): slot i covers key
+  // tiles [0, split[i]) of its row tile when part[i] == 1 and [split[i],
+  // n_tiles) when part[i] == 2, and writes its partial result to workspace
+  // slot (sbi[i] * BG + bg) * 2 + part[i] - 1; part[i] == 0 covers them all.
+  uint8_t part[kMaxOrder];
+  uint8_t sbi[kMaxOrder];
+  uint16_t split[kMaxOrder];
+  float* ws;
 };
 
 // Zero the output rows of heads the router did not keep, for the tokens whose
@@ -167,6 +175,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   const int bg = bid % a.BG;
   const int band = bid / a.BG;
   const int tile = !a.causal ? band : a.n_order ? (int)a.order[band] : a.n_row_tiles - 1 - band;
+  const int part = a.n_order ? (int)a.part[band] : 0;
   // The shared head's problem (uniform per block; only routed launches carry one).
   const bool shared = ROUTED && bg >= a.BG_main;
   const int b = shared ? bg - a.BG_main : bg / a.g;
@@ -181,7 +190,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   const int row0 = tile * kRowsPerBlock;
   if (row0 >= n_rows) return;  // a shared-head problem has T rows, fewer than the routed ones when k > 1
 
-  if (ROUTED && a.zero_unselected && !shared) zero_unselected_rows<D, W>(a, b, gam, row0, n_rows);
+  if (ROUTED && a.zero_unselected && !shared && part <= 1) zero_unselected_rows<D, W>(a, b, gam, row0, n_rows);
 
   // Attention row rho (< n_rows): token, slot, head (a routed row's head is
   // the router's pick) and gate.
@@ -218,6 +227,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   const int t_last = (min(row0 + kRowsPerBlock, n_rows) - 1) / R;
   const int n_keys = a.causal ? t_last + 1 : a.T;
   const int n_tiles = div_up(n_keys, kBN);
+  const int kt_lo = part == 2 ? (int)a.split[band] : 0;
+  const int kt_hi = part == 1 ? (int)a.split[band] : n_tiles;
 
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   uint16_t* const QOw = QO + wave_u * kQElems;
@@ -303,7 +314,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  issue_tile(0, B0{});
+  issue_tile(kt_lo, B0{});
   __syncthreads();
 
   // Q^T fragments: B operand of S^T = K Q^T. Lane half hq holds d in
@@ -319,7 +330,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   auto tile_step = [&](int kt, auto buf) {
     const uint16_t* const Kb = buf.value ? K1 : K0;
     const uint16_t* const Vb = buf.value ? V1 : V0;
-    if (kt + 1 < n_tiles) issue_tile(kt + 1, std::integral_constant<int, 1 - buf.value>{});
+    if (kt + 1 < kt_hi) issue_tile(kt + 1, std::integral_constant<int, 1 - buf.value>{});
     const int key0 = kt * kBN;
     const bool active = wave_has_rows && (!a.causal || key0 <= wt_hi);
     if (active) {
@@ -404,24 +415,35 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
     }
     __syncthreads();
   };
-  for (int kt = 0; kt < n_tiles; kt += 2) {
+  for (int kt = kt_lo; kt < kt_hi; kt += 2) {
     tile_step(kt, B0{});
-    if (kt + 1 < n_tiles) tile_step(kt + 1, B1{});
+    if (kt + 1 < kt_hi) tile_step(kt + 1, B1{});
   }
 
   // Output: each pass stages D*2 bytes of each of the wave's 32 rows in QOw
   // (all of a bf16 row, half of an fp32 row), then stores them row by row, 16
-  // bytes per lane.
+  // bytes per lane. A key-split part stores instead its partial result in its
+  // workspace slot: the unnormalised O rows in fp32, then per row the
+  // reference max m_ref and the sum l (rows past the end included).
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = __int_as_float(tab[l32].w) / l_tot;
+  const bool partial = part != 0;
+  float* const pws =
+      partial ? a.ws + ((size_t)(a.sbi[band] * a.BG + bg) * 2 + part - 1) * ((size_t)kRowsPerBlock * (D + 2))
+              : nullptr;
+  if (partial && hq == 0) {
+    pws[kRowsPerBlock * D + wave * 32 + l32] = m_ref;
+    pws[kRowsPerBlock * (D + 1) + wave * 32 + l32] = l_tot;
+  }
+  const float inv = partial ? 1.0f : __int_as_float(tab[l32].w) / l_tot;
   constexpr int kRowB = L::kPitch * 2;      // staged row pitch, bytes
   constexpr int kG = D * 2 / 16;            // 16-byte granules per staged row
   constexpr int kRowsPer = 64 / kG;         // rows per store instruction
   char* const stage = reinterpret_cast<char*>(QOw);
-  const int n_pass = a.out_bf16 ? 1 : 2;
+  const bool bf16_out = a.out_bf16 && !partial;
+  const int n_pass = bf16_out ? 1 : 2;
   for (int pass = 0; pass < n_pass; ++pass) {
     // o[db][4*i4 + j] holds d = 32db + 8i4 + 4hq + j of this lane's row.
-    if (a.out_bf16) {
+    if (bf16_out) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -451,7 +473,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
       const int gran = lane % kG;
       const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * kRowB + gran * 16);
       const int rr = wrow0 + row;
-      if (rr < n_rows) {
+      if (partial) {
+        *reinterpret_cast<u32x4*>(pws + (size_t)(wave * 32 + row) * D + pass * (D / 2) + gran * 4) = v;
+      } else if (rr < n_rows) {
         const int4 ri = tab[row];
         const int oslot = a.out_slots ? gam * a.R + ri.z : ri.y;
         const size_t orow = shared ? ((size_t)b * a.T + ri.x) * D : b * a.o_b + oslot * a.o_h + ri.x * a.o_t;
@@ -464,6 +488,64 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   }
 }
 
+// Merges the two parts of every key-split row tile. Per row the partial
+// results (m_p, l_p, O_p) over the two key ranges, each taken against its own
+// reference max, combine as the online softmax does within a part:
+//   m = max(m_1, m_2),  w_p = 2^(m_p - m),
+//   O = (w_1 O_1 + w_2 O_2) / (w_1 l_1 + w_2 l_2),
+// then the row's gate and the attention kernel's output layout.
+template <int D, int W, bool ROUTED>
+__global__ __launch_bounds__(256) void split_merge_kernel(KArgs a) {
+  constexpr int kRowsPerBlock = W * 32, kRowsPerSub = 256 / (D / 8), kSubs = kRowsPerBlock / kRowsPerSub;
+  static_assert(kRowsPerBlock % kRowsPerSub == 0, "merge sub-blocks must tile the row tile");
+  const int sub = blockIdx.x % kSubs, sbg = blockIdx.x / kSubs;
+  const int sb = sbg / a.BG, bg = sbg % a.BG;
+  int tile = 0;
+  for (int i = 0; i < a.n_order; ++i)
+    if (a.part[i] == 1 && a.sbi[i] == sb) tile = a.order[i];
+  const int b = bg / a.g, gam = bg - b * a.g;  // split launches carry no shared head
+  const int R = a.R, n_rows = a.T * R, row0 = tile * kRowsPerBlock;
+  const float* const p1 = a.ws + (size_t)(sb * a.BG + bg) * 2 * ((size_t)kRowsPerBlock * (D + 2));
+  const float* const p2 = p1 + (size_t)kRowsPerBlock * (D + 2);
+  {
+    const int row = sub * kRowsPerSub + threadIdx.x / (D / 8), ch = threadIdx.x % (D / 8);
+    const int rho = row0 + row;
+    if (rho >= n_rows) return;
+    const float m1 = p1[kRowsPerBlock * D + row], l1 = p1[kRowsPerBlock * (D + 1) + row];
+    const float m2 = p2[kRowsPerBlock * D + row], l2 = p2[kRowsPerBlock * (D + 1) + row];
+    const float m = fmaxf(m1, m2);
+    const float w1 = fast_exp2(m1 - m), w2 = fast_exp2(m2 - m);
+    const int t = rho / R, slot = rho - t * R;
+    int head;
+    float gate = 1.0f;
+    if (ROUTED) {
+      const size_t o = ((size_t)(b * a.T + t) * a.g + gam) * a.R + slot;
+      head = a.idx[o];
+      gate = a.out_slots ? 1.0f : a.gate[o];
+    } else {
+      head = gam * a.r + slot;
+    }
+    const float sc = gate / (w1 * l1 + w2 * l2);
+    const float4* x1 = reinterpret_cast<const float4*>(p1 + (size_t)row * D + ch * 8);
+    const float4* x2 = reinterpret_cast<const float4*>(p2 + (size_t)row * D + ch * 8);
+    const float4 a0 = x1[0], a1 = x1[1], b0 = x2[0], b1 = x2[1];
+    const float v[8] = {(w1 * a0.x + w2 * b0.x) * sc, (w1 * a0.y + w2 * b0.y) * sc,
+                        (w1 * a0.z + w2 * b0.z) * sc, (w1 * a0.w + w2 * b0.w) * sc,
+                        (w1 * a1.x + w2 * b1.x) * sc, (w1 * a1.y + w2 * b1.y) * sc,
+                        (w1 * a1.z + w2 * b1.z) * sc, (w1 * a1.w + w2 * b1.w) * sc};
+    const int oslot = a.out_slots ? gam * a.R + slot : head;
+    const size_t off = b * a.o_b + oslot * a.o_h + t * a.o_t + ch * 8;
+    if (a.out_bf16) {
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + off) = make_uint4(
+          pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    } else {
+      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.out) + off);
+      dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+      dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
 // Dispatch order of the row-tile bands of a causal grid. The hardware hands
 // blocks to CUs in index order as CUs free up; a band is one row tile of every
 // problem. Heaviest first leaves the last round short of work: at B=4, h=32,
@@ -473,22 +555,59 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
 // bands are kept while they shorten the simulated end. The per-job fixed cost
 // (prologue and epilogue) was fitted by measurement: about 4 tiles of 32 keys.
 // Cached per shape; shapes with more bands keep heaviest first.
+//
+// Key splitting (routed launches given a workspace): when the grid holds less
+// than two blocks per CU, the heaviest row tiles of the upper half of the
+// sequence are split at a key tile into two parts that run as separate jobs,
+// and a second kernel merges their partial results. The split key tile is
+// never past the tile's first token, so every row sees keys in both parts.
+// A split is kept when it shortens the modelled end.
 struct OrderShape {
-  int n_bands, rows, R, T, kBN, BG_main, B_sh, n_cu;
+  int n_bands, rows, R, T, kBN, BG_main, B_sh, n_cu, max_split;
   bool operator<(const OrderShape& o) const {
-    return std::tie(n_bands, rows, R, T, kBN, BG_main, B_sh, n_cu) <
-           std::tie(o.n_bands, o.rows, o.R, o.T, o.kBN, o.BG_main, o.B_sh, o.n_cu);
+    return std::tie(n_bands, rows, R, T, kBN, BG_main, B_sh, n_cu, max_split) <
+           std::tie(o.n_bands, o.rows, o.R, o.T, o.kBN, o.BG_main, o.B_sh, o.n_cu, o.max_split);
   }
 };
+
+struct Slot {
+  uint16_t tile, split;
+  uint8_t part, sbi;
+};
+
+// Key tiles of row tile i of a problem with T*R rows (R per token), and the
+// key tile at which it may be split.
+struct BandKeys {
+  int n_tiles, split;
+};
+BandKeys band_keys(int i, int rows, int R, int T, int kBN) {
+  const int n_rows = T * R, row0 = i * rows;
+  if (row0 >= n_rows) return {0, 0};
+  const int t_first = row0 / R, t_last = (std::min(row0 + rows, n_rows) - 1) / R;
+  const int n_tiles = div_up(t_last + 1, kBN);
+  return {n_tiles, std::min(n_tiles / 2, t_first / kBN)};
+}
+
+// Row tiles that may be split in one launch (0 when the grid has two or more
+// blocks per CU): those of the upper half with a split point inside.
+int split_cap(int n_bands, int rows, int R, int T, int kBN, int BG, int n_cu) {
+  if ((long long)n_bands * BG >= 2ll * n_cu || n_bands >= kMaxOrder) return 0;
+  int eligible = 0;
+  for (int i = n_bands / 2; i < n_bands; ++i) {
+    const BandKeys k = band_keys(i, rows, R, T, kBN);
+    if (k.split >= 1 && k.n_tiles - k.split >= 1) ++eligible;
+  }
+  return std::min(eligible, kMaxOrder - n_bands);
+}
 
 double simulate_dispatch(const std::vector<int>& order, const std::vector<double>& cost_main,
                          const std::vector<double>& cost_sh, int per_main, int per_sh, int n_cu) {
   std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
   for (int i = 0; i < n_cu; ++i) free_at.push(0.0);
   double end = 0.0;
-  for (int band : order)
+  for (int slot : order)
     for (int j = 0; j < per_main + per_sh; ++j) {
-      const double t = free_at.top() + (j < per_main ? cost_main[band] : cost_sh[band]);
+      const double t = free_at.top() + (j < per_main ? cost_main[slot] : cost_sh[slot]);
       free_at.pop();
       free_at.push(t);
       end = std::max(end, t);
@@ -496,20 +615,16 @@ double simulate_dispatch(const std::vector<int>& order, const std::vector<double
   return end;
 }
 
-std::vector<uint16_t> plan_order(const OrderShape& s) {
-  // Key tiles of row tile i of a problem with n_rows = T*R rows, R per token.
-  auto cost = [&](int i, int R, double fixed) {
-    const int n_rows = s.T * R, row0 = i * s.rows;
-    if (row0 >= n_rows) return 0.0;
-    const int t_last = (std::min(row0 + s.rows, n_rows) - 1) / R;
-    return (double)div_up(t_last + 1, s.kBN) + fixed;
-  };
+std::vector<Slot> plan_order(const OrderShape& s) {
   const double fixed = 128.0 / s.kBN;  // ≈ 4 tiles of 32 keys
-  std::vector<double> cost_main(s.n_bands), cost_sh(s.n_bands);
-  for (int i = 0; i < s.n_bands; ++i) {
-    cost_main[i] = cost(i, s.R, fixed);
-    cost_sh[i] = cost(i, 1, fixed);
-  }
+  std::vector<Slot> slots;
+  for (int i = 0; i < s.n_bands; ++i) slots.push_back(Slot{(uint16_t)i, 0, 0, 0});
+  auto slot_cost = [&](const Slot& sl, int R) {
+    const BandKeys k = band_keys(sl.tile, s.rows, R, s.T, s.kBN);
+    if (k.n_tiles == 0) return 0.0;
+    const int n = sl.part == 0 ? k.n_tiles : sl.part == 1 ? sl.split : k.n_tiles - sl.split;
+    return (double)n + fixed;
+  };
   // With whole problems per XCD slice (blocks go to XCDs round-robin), one
   // eighth of the CUs and of each band is an exact model.
   int per_main = s.BG_main, per_sh = s.B_sh, n_cu = s.n_cu;
@@ -518,13 +633,58 @@ std::vector<uint16_t> plan_order(const OrderShape& s) {
     per_sh /= 8;
     n_cu /= 8;
   }
-  std::vector<int> order(s.n_bands);
-  for (int i = 0; i < s.n_bands; ++i) order[i] = s.n_bands - 1 - i;  // heaviest first
+  std::vector<double> cost_main, cost_sh;
+  auto costs = [&]() {
+    cost_main.assign(slots.size(), 0.0);
+    cost_sh.assign(slots.size(), 0.0);
+    for (size_t i = 0; i < slots.size(); ++i) {
+      cost_main[i] = slot_cost(slots[i], s.R);
+      cost_sh[i] = slot_cost(slots[i], 1);
+    }
+  };
+  auto heaviest_first = [&]() {
+    std::vector<int> order(slots.size());
+    for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return cost_main[x] > cost_main[y]; });
+    return order;
+  };
+  // Splits, heaviest row tile first, kept while the end shortens.
+  if (s.max_split > 0 && s.B_sh == 0) {
+    std::vector<int> cand;
+    for (int i = s.n_bands / 2; i < s.n_bands; ++i) {
+      const BandKeys k = band_keys(i, s.rows, s.R, s.T, s.kBN);
+      if (k.split >= 1 && k.n_tiles - k.split >= 1) cand.push_back(i);
+    }
+    std::stable_sort(cand.begin(), cand.end(), [&](int x, int y) {
+      return band_keys(x, s.rows, s.R, s.T, s.kBN).n_tiles > band_keys(y, s.rows, s.R, s.T, s.kBN).n_tiles;
+    });
+    costs();
+    double best = simulate_dispatch(heaviest_first(), cost_main, cost_sh, per_main, per_sh, n_cu);
+    int n_split = 0;
+    for (int i : cand) {
+      if (n_split == s.max_split) break;
+      const uint16_t sp = (uint16_t)band_keys(i, s.rows, s.R, s.T, s.kBN).split;
+      std::vector<Slot> keep = slots;
+      for (auto& sl : slots)
+        if (sl.tile == i) sl = Slot{(uint16_t)i, sp, 1, (uint8_t)n_split};
+      slots.push_back(Slot{(uint16_t)i, sp, 2, (uint8_t)n_split});
+      costs();
+      const double m = simulate_dispatch(heaviest_first(), cost_main, cost_sh, per_main, per_sh, n_cu);
+      if (m < best - 1e-9) {
+        best = m;
+        ++n_split;
+      } else {
+        slots = keep;
+      }
+    }
+  }
+  costs();
+  std::vector<int> order = heaviest_first();
   double best = simulate_dispatch(order, cost_main, cost_sh, per_main, per_sh, n_cu);
   for (int pass = 0; pass < 4; ++pass) {
     bool improved = false;
-    for (int i = 0; i < s.n_bands; ++i)
-      for (int j = i + 1; j < s.n_bands; ++j) {
+    for (size_t i = 0; i < order.size(); ++i)
+      for (size_t j = i + 1; j < order.size(); ++j) {
         std::swap(order[i], order[j]);
         const double m = simulate_dispatch(order, cost_main, cost_sh, per_main, per_sh, n_cu);
         if (m < best - 1e-9) {
@@ -536,31 +696,71 @@ std::vector<uint16_t> plan_order(const OrderShape& s) {
       }
     if (!improved) break;
   }
-  return std::vector<uint16_t>(order.begin(), order.end());
+  std::vector<Slot> out;
+  for (int i : order) out.push_back(slots[i]);
+  return out;
 }
 
 void set_order(KArgs& a, const OrderShape& s) {
   a.n_order = 0;
   if (!a.causal || s.n_bands < 2 || s.n_bands > kMaxOrder) return;
   static std::mutex mu;
-  static std::map<OrderShape, std::vector<uint16_t>> cache;
+  static std::map<OrderShape, std::vector<Slot>> cache;
   std::lock_guard<std::mutex> lock(mu);
   auto it = cache.find(s);
   if (it == cache.end()) it = cache.emplace(s, plan_order(s)).first;
-  std::copy(it->second.begin(), it->second.end(), a.order);
-  a.n_order = s.n_bands;
+  const std::vector<Slot>& v = it->second;
+  for (size_t i = 0; i < v.size(); ++i) {
+    a.order[i] = v[i].tile;
+    a.part[i] = v[i].part;
+    a.sbi[i] = v[i].sbi;
+    a.split[i] = v[i].split;
+  }
+  a.n_order = (int)v.size();
 }
 
 template <int D, int W, int BN, int OCC>
 hipError_t launch_dw(KArgs a, const AttnParams& p, hipStream_t stream, int n_cu) {
   a.n_row_tiles = div_up(p.T * p.R, W * 32);
-  set_order(a, OrderShape{a.n_row_tiles, W * 32, p.R, p.T, BN, a.BG_main, a.BG - a.BG_main, n_cu});
-  const dim3 grid(a.n_row_tiles * a.BG), block(W * 64);
+  const int max_split =
+      p.split_ws ? split_cap(a.n_row_tiles, W * 32, p.R, p.T, BN, a.BG_main, n_cu) : 0;
+  set_order(a, OrderShape{a.n_row_tiles, W * 32, p.R, p.T, BN, a.BG_main, a.BG - a.BG_main, n_cu,
+                          a.BG == a.BG_main ? max_split : 0});
+  a.ws = static_cast<float*>(p.split_ws);
+  int n_split = 0;
+  for (int i = 0; i < a.n_order; ++i) n_split += a.part[i] == 1;
+  const dim3 grid((a.n_order ? a.n_order : a.n_row_tiles) * a.BG), block(W * 64);
   if (p.idx)
     hipLaunchKernelGGL((attn_bf16_kernel<D, W, BN, OCC, true>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<D, W, BN, OCC, false>), grid, block, 0, stream, a);
+  if (n_split == 0) return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // One merge block per 256 (row, 8-column chunk) items of a split tile.
+  const dim3 merge_grid(n_split * a.BG * (W * 32 * (D / 8) / 256));
+  if (p.idx)
+    hipLaunchKernelGGL((split_merge_kernel<D, W, true>), merge_grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((split_merge_kernel<D, W, false>), merge_grid, dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+// CU count of the current device (256 when it cannot be read).
+int device_cus() {
+  int n_cu = 256, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    n_cu = 256;
+  return n_cu;
+}
+
+// The configuration a launch takes: 12 waves / 32-key tiles when the grid
+// gives every CU at least two 12-wave blocks' worth of waves, else 8 waves /
+// 64-key tiles.
+bool large_config(int BG, int T, int R, int n_cu) {
+  const long long large_grid = (long long)BG * div_up(T * R, kWavesLarge * 32);
+  return large_grid * kWavesLarge >= 24ll * n_cu;
 }
 
 template <int D>
@@ -596,12 +796,9 @@ hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
   a.o_b = p.o_b ? p.o_b : (size_t)p.h * TD;
   a.o_h = p.o_h ? p.o_h : TD;
   a.o_t = p.o_t ? p.o_t : D;
-  int n_cu = 256, dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    n_cu = 256;
-  const long long large_grid = (long long)a.BG * div_up(p.T * p.R, kWavesLarge * 32);
-  if (large_grid * kWavesLarge >= 24ll * n_cu)
+  const int n_cu = device_cus();
+  if (p.split_ws && p.q_shared) return hipErrorInvalidValue;  // key splitting is for plain routed launches
+  if (large_config(a.BG, p.T, p.R, n_cu))
     return launch_dw<D, kWavesLarge, kBNLarge, kOccLarge>(a, p, stream, n_cu);
   return launch_dw<D, kWavesSmall, kBNSmall, kOccSmall>(a, p, stream, n_cu);
 }
@@ -609,6 +806,16 @@ hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
 }  // namespace
 
 bool attn_bf16_supports(int d) { return d == 64 || d == 128; }
+
+size_t attn_bf16_split_ws_bytes(int B, int g, int T, int d, int R, int causal) {
+  if (!causal || B <= 0 || T <= 0) return 0;
+  const int n_cu = device_cus(), BG = B * g;
+  const bool large = large_config(BG, T, R, n_cu);
+  const int W = large ? kWavesLarge : kWavesSmall, kBN = large ? kBNLarge : kBNSmall;
+  const int n_bands = div_up(T * R, W * 32);
+  const int cap = split_cap(n_bands, W * 32, R, T, kBN, BG, n_cu);
+  return (size_t)cap * BG * 2 * (size_t)(W * 32) * (d + 2) * sizeof(float);
+}
 
 hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
   switch (p.d) {

@@ -37,6 +37,10 @@ struct AttnParams {
   const void* q_shared;
   void* out_shared;
   int shared_kv;
+  // Routed causal launches (bf16 kernel only; null: none): workspace of at
+  // least attn_bf16_split_ws_bytes(...) bytes for the partial results of
+  // key-split row tiles.
+  void* split_ws;
 };
 
 struct RouterParams {
@@ -89,6 +93,9 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
 // Head dims with a bf16 MFMA prefill kernel / an fp32 kernel / a decode kernel.
 bool attn_bf16_supports(int d);
+// Workspace bytes a routed causal bf16 launch of this shape may use for key splits
+// (0 when it would split nothing); R is the number of rows per token.
+size_t attn_bf16_split_ws_bytes(int B, int g, int T, int d, int R, int causal);
 bool attn_f32_supports(int d);
 bool decode_supports(int d);
 bool router_proj_supports(int d_model, int h);

@@ -213,14 +213,30 @@ gqa_status gqe_routed_decode(const void* q, const void* k_cache, const void* v_c
  *   out [B, h, T, d] out_dtype, written in full: out[b, i, t] is
  *           gate * (GQA attention row of head i at token t, dense K/V) when
  *           the router kept head i for token t, and 0 otherwise.
- * Supported: as gqa_prefill.
+ *   workspace: null, or device memory (16-byte aligned) of at least
+ *           gqe_workspace_bytes(...) bytes; its contents need no
+ *           initialisation and are not kept between calls. Calls that
+ *           overlap on one workspace race.
+ * Supported: as gqa_prefill. Returns GQA_ERR_WORKSPACE when a non-null
+ * workspace is smaller than gqe_workspace_bytes(...).
  */
 gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v,
                               const float* router_logits, int top_k,
                               void* out, int32_t* topk_idx, float* topk_gate,
                               int B, int h, int g, int T, int d,
                               gqa_dtype in_dtype, gqa_dtype out_dtype,
-                              float scale, int causal, void* stream);
+                              float scale, int causal,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace gqe_routed_prefill can use at this shape (causal
+ * bf16 on the current device; 0 when it would use none). With the workspace,
+ * a launch whose grid is less than two blocks per CU may split the key range
+ * of its heaviest causal row tiles over two jobs whose partial results (the
+ * row max, the row sum and the unnormalised output, fp32) are merged by a
+ * second kernel: the same result, with the work spread over the chip.
+ */
+size_t gqe_workspace_bytes(int B, int h, int g, int T, int d, int top_k);
 
 /*
  * KV-cache size in bytes for one layer: 2 (keys and values) * n_kv * d * T

@@ -30,14 +30,14 @@ def _declared_functions():
 
 def test_header_symbols_exported():
     names = _declared_functions()
-    assert {"gqa_prefill", "gqa_decode", "gqe_routed_prefill"} <= set(names)
+    assert {"gqa_prefill", "gqa_decode", "gqe_routed_prefill", "gqe_workspace_bytes"} <= set(names)
     so = ctypes.CDLL(gq.lib_path)
     for n in names:
         assert hasattr(so, n), f"{n} declared in gqa.h but not exported"
 
 
 def test_abi_version_and_status_strings():
-    assert gq.abi_version() == 1
+    assert gq.abi_version() == 2
     for s in range(6):
         assert gq.status_string(s)
     assert gq.status_string(99) == "unknown status"
@@ -101,11 +101,12 @@ def test_decode_rejects(kw, status):
 
 def _gqe(**kw):
     a = dict(q=P, k=P, v=P, lg=P, k_top=1, out=P, idx=P, gate=P, B=1, h=8, g=2, T=16, d=128,
-             i=BF16, o=BF16, scale=0.088, causal=1, stream=None)
+             i=BF16, o=BF16, scale=0.088, causal=1, ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib.gqe_routed_prefill(a["q"], a["k"], a["v"], a["lg"], a["k_top"], a["out"],
                                   a["idx"], a["gate"], a["B"], a["h"], a["g"], a["T"], a["d"],
-                                  a["i"], a["o"], a["scale"], a["causal"], a["stream"])
+                                  a["i"], a["o"], a["scale"], a["causal"], a["ws"], a["wsb"],
+                                  a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -114,9 +115,26 @@ def _gqe(**kw):
     (dict(lg=None), INVALID),
     (dict(idx=None), INVALID),
     (dict(h=130, g=1, k_top=1), UNSUPPORTED),
+    (dict(ws=P + 8, wsb=1 << 20), INVALID),   # workspace not 16-byte aligned
 ])
 def test_gqe_rejects(kw, status):
     assert _gqe(**kw) == status
+
+
+def test_gqe_workspace_bytes():
+    """Key splitting is planned only for causal grids of less than two blocks
+    per CU, upper-half row tiles only: the GQE workload (B=2, T=4096, h=32, g=8,
+    k=1) needs a workspace, large grids need none, invalid shapes return 0.
+    Without a GPU the size is computed for 256 CUs (MI355X)."""
+    small = gq.gqe_workspace_bytes(2, 32, 8, 4096, 128, 1)
+    assert small > 0 and small % 16 == 0
+    # one split row tile holds its two partial results: 2 * rows * (d + 2) floats per problem
+    per_tile = 2 * 2 * 8 * 256 * (128 + 2) * 4
+    assert small % per_tile == 0 and small // per_tile <= 8
+    assert gq.gqe_workspace_bytes(64, 32, 8, 4096, 128, 1) == 0   # 2048+ blocks: no split
+    assert gq.gqe_workspace_bytes(2, 32, 8, 4096, 128, 5) == 0    # top_k > h/g
+    assert gq.gqe_workspace_bytes(2, 32, 8, 4096, 96, 1) == 0     # d not run on the bf16 kernel
+    assert gq.gqe_workspace_bytes(0, 32, 8, 4096, 128, 1) == 0
 
 
 def _gqe_decode(**kw):

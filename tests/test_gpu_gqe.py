@@ -12,12 +12,12 @@ from workloads import WORKLOADS, gqe_inputs, gqe_sweep_points, prefill_inputs
 pytestmark = pytest.mark.gpu
 
 
-def _run(q, k, v, lg, top_k, causal=True, out_dtype=torch.float32):
+def _run(q, k, v, lg, top_k, causal=True, out_dtype=torch.float32, workspace=True):
     import gqa_routed_query_amd as gq
 
     d = dev()
     res = gq.gqe_routed_prefill(q.to(d), k.to(d), v.to(d), lg.to(d), top_k, causal=causal,
-                                out_dtype=out_dtype)
+                                out_dtype=out_dtype, workspace=workspace)
     torch.cuda.synchronize()
     return res
 
@@ -46,13 +46,14 @@ def test_gqe_shapes(B, h, g, T, d, top_k, ties, dt):
 
 
 def test_gqe_top1_rows_equal_dense_rows():
-    """With k = 1 the gate is 1 and a kept row is the dense GQA row."""
+    """With k = 1 the gate is 1 and a kept row is the dense GQA row, to the bit
+    when both run the same arithmetic (no workspace: no key splits)."""
     import gqa_routed_query_amd as gq
 
     d = dev()
     say("gqe k=1 vs dense prefill")
     q, k, v, lg = gqe_inputs(1, 8, 2, 260, 128, "bf16", seed=61)
-    out, idx, gate = _run(q, k, v, lg, 1)
+    out, idx, gate = _run(q, k, v, lg, 1, workspace=None)
     dense = gq.gqa_prefill(q.to(d), k.to(d), v.to(d), causal=True, out_dtype=torch.float32)
     assert bool((gate == 1.0).all())
     idx_c = idx.cpu()
@@ -117,6 +118,43 @@ def test_gqe_large_grid_ragged():
                     i = int(ridx[bb, t, gam, j])
                     ref = rgate[bb, t, gam, j] * oracle.gqa_ref_row(qc, kc, vc, bb, i, t)
                     worst = max(worst, float(np.abs(np64(out[bb, i, t]) - ref).max()))
+    assert worst <= TOL_BF16, worst
+
+
+@pytest.mark.parametrize("B,h,g,T,d,top_k,out_dt", [
+    (2, 32, 8, 4096, 128, 1, torch.bfloat16),   # the GQE workload at k=1: one round of jobs
+    (2, 8, 2, 300, 128, 2, torch.float32),
+    (1, 12, 4, 333, 64, 3, torch.bfloat16),
+])
+def test_gqe_key_split_matches_unsplit(B, h, g, T, d, top_k, out_dt):
+    """With a workspace, a causal grid of less than two blocks per CU splits the
+    key range of its heaviest row tiles over two jobs and merges their partial
+    results. The router outputs are identical, and the output equals the launch
+    without a workspace within the bf16 tolerance (as it equals the oracle)."""
+    import gqa_routed_query_amd as gq
+
+    dv = dev()
+    say(f"gqe key split B={B} h={h} g={g} T={T} d={d} k={top_k} out={out_dt}")
+    assert gq.gqe_workspace_bytes(B, h, g, T, d, top_k) > 0
+    q, k, v, lg = gqe_inputs(B, h, g, T, d, "bf16", seed=300 + T, device=dv)
+    a, ia, ga = gq.gqe_routed_prefill(q, k, v, lg, top_k, out_dtype=out_dt, workspace=True)
+    b, ib, gb = gq.gqe_routed_prefill(q, k, v, lg, top_k, out_dtype=out_dt, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(ia, ib) and torch.equal(ga, gb)
+    assert torch.equal(a == 0, b == 0)
+    # The probabilities are rounded to bf16 against each part's own reference
+    # max, so the two launches differ at bf16 precision even with fp32 output.
+    assert max_abs(a, b) <= TOL_BF16, max_abs(a, b)
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    ridx, rgate = ia.cpu().numpy(), ga.cpu().numpy()
+    worst = 0.0
+    for t in sample_tokens(T, 10, seed=T):
+        for bb in {0, B - 1}:
+            for gam in (0, g - 1):
+                for j in range(top_k):
+                    i = int(ridx[bb, t, gam, j])
+                    ref = rgate[bb, t, gam, j] * oracle.gqa_ref_row(qc, kc, vc, bb, i, t)
+                    worst = max(worst, float(np.abs(np64(a[bb, i, t]) - ref).max()))
     assert worst <= TOL_BF16, worst
 
 

@@ -52,7 +52,8 @@ def test_gqe_build_wsum_is_routed_output_summed_over_group():
     say("gqe build vs routed prefill")
     q, qs, k, v, lg = _inputs(B, h, g, T, d, seed=920, device=dv)
     _, wsum, _, idx, gate = gq.gqe_prefill_build(q, qs, k, v, lg, 2, out_dtype=torch.float32)
-    out, idx2, gate2 = gq.gqe_routed_prefill(q, k, v, lg, 2, out_dtype=torch.float32)
+    out, idx2, gate2 = gq.gqe_routed_prefill(q, k, v, lg, 2, out_dtype=torch.float32,
+                                             workspace=None)  # same arithmetic: no key splits
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2) and torch.equal(gate, gate2)
     grp = out.view(B, g, h // g, T, d).sum(2).permute(0, 2, 1, 3)   # [B,T,g,d]
