@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the peak microbenchmarks (HBM read stream, MFMA-only loop)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the sweeps outside the step (KV-group decode, GQE vs GQA over T)")
     ap.add_argument("--only", choices=["prefill", "decode", "gqe", "copy"], default=None,
@@ -352,6 +354,11 @@ def main():
             del q, k, v, lg, out
             torch.cuda.empty_cache()
 
+    # ---- measured peaks: the rates the path is compared with besides the datasheet ----
+    peaks = None
+    if args.only is None and not args.no_peaks:
+        peaks = measured_peaks(torch, gq, dev)
+
     # ---- CPU oracle baseline on a bounded sample of the prefill workload ----
     cpu = None
     if run_prefill and not args.no_cpu:
@@ -388,6 +395,11 @@ def main():
             "frac": p["tflops"] / PEAK_BF16_TFLOPS,
             "traffic": traffic_for("prefill"),
         }
+        if peaks:
+            line["roofline"]["measured_peak"] = peaks["mfma_bf16"]["TFLOPs"]
+            line["roofline"]["frac_measured_peak"] = p["tflops"] / peaks["mfma_bf16"]["TFLOPs"]
+        line["prefill"] = {"mean_us": p["mean_ms"] * 1e3, "median_us": p["median_ms"] * 1e3,
+                           "min_us": p["min_ms"] * 1e3, "flops_per_launch": p["flops_per_launch"]}
     if "decode" in res:
         dd = res["decode"]
         line["decode"] = {
@@ -396,8 +408,12 @@ def main():
                          "bound": "hbm", "achieved": dd["GBps"], "peak": PEAK_HBM_GBPS,
                          "unit": "GB/s", "frac": dd["frac_peak"],
                          "traffic": traffic_for("decode")},
-            "mean_us": dd["mean_ms"] * 1e3, "bytes_per_call": dd["bytes_per_call"],
+            "mean_us": dd["mean_ms"] * 1e3, "median_us": dd["median_ms"] * 1e3,
+            "min_us": dd["min_ms"] * 1e3, "bytes_per_call": dd["bytes_per_call"],
         }
+        if peaks:
+            line["decode"]["roofline"]["measured_peak"] = peaks["hbm_read"]["GBps"]
+            line["decode"]["roofline"]["frac_measured_peak"] = dd["GBps"] / peaks["hbm_read"]["GBps"]
     if "gqe" in res:
         line["gqe"] = {k: {"tflops": v["tflops"], "frac": v["frac_peak"],
                            "mean_us": v["mean_ms"] * 1e3,
@@ -412,9 +428,69 @@ def main():
         line["gqe_decode"] = gdec
     if grouter:
         line["gqe_router"] = dict(grouter, n_tokens=wg.B * wg.T, d_model=ROUTER_D_MODEL, h=wg.h, g=wg.g)
+    if peaks:
+        line["measured_peaks"] = peaks
     if cpu:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
+
+
+def measured_peaks(torch, gq, dev):
+    """The library's peak microbenchmarks, each timed as the median of 10
+    launches with HIP events: an HBM read of a 4 GiB buffer (16 times the
+    Infinity Cache) and the MFMA-only loop, once as long as a prefill launch
+    and once long enough for the clock to settle under MFMA load. Also the
+    clocks and power cap rocm-smi reports."""
+    out = {}
+    buf = torch.randint(0, 256, (1 << 32,), dtype=torch.uint8, device=dev)
+    xo = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        gq.peak_hbm_read(buf, xo)
+    t = Timer(torch)
+    for _ in range(10):
+        with t:
+            gq.peak_hbm_read(buf, xo)
+    torch.cuda.synchronize()
+    ms = sorted(t.ms())
+    out["hbm_read"] = {"GBps": buf.numel() / (ms[5] * 1e-3) / 1e9, "bytes": buf.numel(),
+                       "median_us": ms[5] * 1e3, "min_us": ms[0] * 1e3}
+    ops = torch.randn(1024, device=dev).to(torch.bfloat16)
+    so = torch.zeros(1, dtype=torch.float32, device=dev)
+    # 1000 rounds last about as long as one prefill launch (~150 us); 40000
+    # rounds (~6 ms) show the rate once the clock has settled under MFMA load.
+    for key, iters in (("mfma_bf16", 1000), ("mfma_bf16_sustained", 40000)):
+        for _ in range(3):
+            gq.peak_mfma_bf16(ops, iters, so)
+        t = Timer(torch)
+        flops = 0.0
+        for _ in range(10):
+            gq.peak_hbm_read(buf[: 1 << 30], xo)  # as in the bench step: HBM-bound work between launches
+            with t:
+                _, flops = gq.peak_mfma_bf16(ops, iters, so)
+        torch.cuda.synchronize()
+        ms = sorted(t.ms())
+        out[key] = {"TFLOPs": flops / (ms[5] * 1e-3) / 1e12, "flops": flops, "iters": iters,
+                    "median_us": ms[5] * 1e3, "min_us": ms[0] * 1e3}
+    del buf
+    torch.cuda.empty_cache()
+    log(f"measured peaks: HBM read {out['hbm_read']['GBps']:.0f} GB/s, "
+        f"bf16 MFMA {out['mfma_bf16']['TFLOPs']:.0f} TFLOP/s "
+        f"({out['mfma_bf16_sustained']['TFLOPs']:.0f} sustained)")
+    out["rocm_smi"] = rocm_smi_clocks()
+    return out
+
+
+def rocm_smi_clocks():
+    """sclk/mclk and power lines of rocm-smi (None where it is unavailable)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showmaxpower"],
+                           capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    keep = ("sclk", "mclk", "fclk", "power", "Power")
+    lines = [ln.strip() for ln in r.stdout.splitlines() if any(k in ln for k in keep)]
+    return lines or None
 
 
 def cpu_baseline(pq, pk, pv, wp):

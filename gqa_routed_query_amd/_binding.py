@@ -55,6 +55,10 @@ def _load():
     lib.gqe_routed_decode.restype = i32
     lib.gqe_routed_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32,
                                       i32, i32, i32, f32, vp, sz, vp]
+    lib.gqa_peak_hbm_read.restype = i32
+    lib.gqa_peak_hbm_read.argtypes = [vp, sz, vp, vp]
+    lib.gqa_peak_mfma_bf16.restype = i32
+    lib.gqa_peak_mfma_bf16.argtypes = [vp, i32, vp, ctypes.POINTER(ctypes.c_double), vp]
     lib.gqe_prefill_build.restype = i32
     lib.gqe_prefill_build.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, i32, i32,
                                       i32, i32, i32, i32, i32, f32, i32, vp]
@@ -294,6 +298,39 @@ def gqe_router(x, w_r, g: int, top_k: int, return_logits: bool = True):
                          gate.data_ptr(), n_tok, d_model, h, int(g), _dt(x, "x"), _stream(dev))
     _check("gqe_router", st)
     return logits, idx, gate
+
+
+def peak_hbm_read(buf, xor_out=None):
+    """Peak microbenchmark: read every 16-byte word of buf (a contiguous device
+    tensor, nbytes a multiple of 16) once. Returns xor_out, an int32 [1] device
+    tensor into which the XOR of all 32-bit words of buf is folded (zeroed here
+    when not given)."""
+    dev = _dev(buf)
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    if xor_out is None:
+        xor_out = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = _lib.gqa_peak_hbm_read(buf.data_ptr(), buf.numel() * buf.element_size(), xor_out.data_ptr(),
+                                _stream(dev))
+    _check("gqa_peak_hbm_read", st)
+    return xor_out
+
+
+def peak_mfma_bf16(operands, iters: int, sum_out=None):
+    """Peak microbenchmark: the MFMA-only loop. operands: bf16 device tensor of
+    1024 values (64 A fragments of 8, then 64 B fragments). Returns (sum_out,
+    flops): sum_out, a float32 [1] device tensor, receives the sum of all
+    accumulators; flops is the work the launch performs."""
+    dev = _dev(operands)
+    if operands.dtype != torch.bfloat16 or operands.numel() != 1024 or not operands.is_contiguous():
+        raise ValueError("operands must be 1024 contiguous bf16 values")
+    if sum_out is None:
+        sum_out = torch.zeros(1, dtype=torch.float32, device=dev)
+    flops = ctypes.c_double(0.0)
+    st = _lib.gqa_peak_mfma_bf16(operands.data_ptr(), int(iters), sum_out.data_ptr(), ctypes.byref(flops),
+                                 _stream(dev))
+    _check("gqa_peak_mfma_bf16", st)
+    return sum_out, flops.value
 
 
 def gqe_prefill_build(q, q_shared, k, v, router_logits, top_k: int, shared_kv: int = 0,

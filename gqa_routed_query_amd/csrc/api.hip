@@ -325,4 +325,29 @@ gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v, const
   return hip_status(e, "gqe routed attention launch");
 }
 
+gqa_status gqa_peak_hbm_read(const void* buf, size_t bytes, uint32_t* xor_out, void* stream) {
+  g_last_error[0] = '\0';
+  if (bytes % 16 != 0) return fail(GQA_ERR_INVALID_ARG, "bytes=%zu must be a multiple of 16", bytes);
+  if (bytes == 0) return GQA_OK;
+  if (!buf || !xor_out) return fail(GQA_ERR_INVALID_ARG, "null buffer or result pointer");
+  if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(xor_out) & 3u))
+    return fail(GQA_ERR_INVALID_ARG, "buf must be 16-byte and xor_out 4-byte aligned");
+  gqa_status s = check_device();
+  if (s != GQA_OK) return s;
+  return hip_status(gqa::launch_peak_hbm_read(buf, bytes, xor_out, static_cast<hipStream_t>(stream)),
+                    "gqa_peak_hbm_read launch");
+}
+
+gqa_status gqa_peak_mfma_bf16(const void* operands, int iters, float* sum_out, double* flops, void* stream) {
+  g_last_error[0] = '\0';
+  if (iters < 1) return fail(GQA_ERR_INVALID_ARG, "iters=%d must be >= 1", iters);
+  if (!operands || !sum_out || !flops) return fail(GQA_ERR_INVALID_ARG, "null operands, sum or flops pointer");
+  if (!aligned16(operands) || (reinterpret_cast<uintptr_t>(sum_out) & 3u))
+    return fail(GQA_ERR_INVALID_ARG, "operands must be 16-byte and sum_out 4-byte aligned");
+  gqa_status s = check_device();
+  if (s != GQA_OK) return s;
+  return hip_status(gqa::launch_peak_mfma_bf16(operands, iters, sum_out, flops, static_cast<hipStream_t>(stream)),
+                    "gqa_peak_mfma_bf16 launch");
+}
+
 }  // extern "C"

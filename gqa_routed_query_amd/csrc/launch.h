@@ -90,6 +90,11 @@ hipError_t launch_router(const RouterParams& p, hipStream_t stream);
 hipError_t launch_router_proj(const RouterProjParams& p, hipStream_t stream);
 hipError_t launch_wsum(const WsumParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+// Peak microbenchmarks: read `bytes` (a multiple of 16) of buf once and XOR
+// all 32-bit words into *x_out; run the MFMA-only loop, add the sum of its
+// accumulators to *sum_out and report the flops it performs.
+hipError_t launch_peak_hbm_read(const void* buf, size_t bytes, unsigned* x_out, hipStream_t stream);
+hipError_t launch_peak_mfma_bf16(const void* operands, int iters, float* sum_out, double* flops, hipStream_t stream);
 
 // Head dims with a bf16 MFMA prefill kernel / an fp32 kernel / a decode kernel.
 bool attn_bf16_supports(int d);

@@ -251,6 +251,37 @@ const char* gqa_status_string(gqa_status status);
 /* Detail message of the calling thread's last failed call ("" if none). */
 const char* gqa_last_error(void);
 
+/*
+ * Peak microbenchmarks: measurement support, not part of the attention path.
+ * They give the rates the path's kernels are compared with besides the
+ * datasheet peaks (HBM 8 TB/s, dense bf16 MFMA 2.5 PFLOP/s). The caller times
+ * them (events on `stream`).
+ *
+ * gqa_peak_hbm_read: reads every 16-byte word of buf once, with the whole
+ * chip, and XORs all 32-bit words of it into *xor_out (device memory; the
+ * caller sets its start value, 0 for the plain XOR of the buffer).
+ *   buf      device memory, 16-byte aligned; bytes a multiple of 16 (0: no-op).
+ * Errors: GQA_ERR_INVALID_ARG (size, null or misaligned pointer),
+ * GQA_ERR_NO_DEVICE, GQA_ERR_HIP.
+ */
+gqa_status gqa_peak_hbm_read(const void* buf, size_t bytes, uint32_t* xor_out, void* stream);
+
+/*
+ * gqa_peak_mfma_bf16: iters rounds of four independent
+ * v_mfma_f32_32x32x16_bf16 per wave, two waves on every SIMD of the device,
+ * on register operands only (no memory traffic in the loop).
+ *   operands  device memory, 16-byte aligned, 2 KiB: 64 bf16x8 A fragments
+ *             (lane l: row l%32, k = 8*(l/32) .. +7 of a 32x16 A) and then 64
+ *             B fragments (lane l: column l%32, the same k). Random values
+ *             give the power-limited rate of real data.
+ *   sum_out   device float: the sum of all accumulators is added to it,
+ *             i.e. (waves * 4 * iters) * sum(A B).
+ *   flops     host double, written: the flops the launch performs.
+ * Errors: GQA_ERR_INVALID_ARG (iters < 1, null or misaligned pointer),
+ * GQA_ERR_NO_DEVICE, GQA_ERR_HIP.
+ */
+gqa_status gqa_peak_mfma_bf16(const void* operands, int iters, float* sum_out, double* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -217,6 +217,21 @@ def test_gqe_decode_empty_batch_is_ok():
     assert _gqe_decode(B=0, q=None, lg=None) == OK
 
 
+def test_peak_probes_reject_bad_args():
+    fl = ctypes.c_double(0.0)
+    assert lib.gqa_peak_hbm_read(P, 15, P, None) == INVALID        # not a multiple of 16
+    assert lib.gqa_peak_hbm_read(None, 16, P, None) == INVALID     # null buffer
+    assert lib.gqa_peak_hbm_read(P, 16, None, None) == INVALID     # null result
+    assert lib.gqa_peak_hbm_read(P + 8, 16, P, None) == INVALID    # misaligned buffer
+    assert lib.gqa_peak_hbm_read(P, 16, P + 2, None) == INVALID    # misaligned result
+    assert lib.gqa_peak_hbm_read(None, 0, None, None) == OK        # nothing to read
+    assert lib.gqa_peak_mfma_bf16(P, 0, P, ctypes.byref(fl), None) == INVALID
+    assert lib.gqa_peak_mfma_bf16(None, 1, P, ctypes.byref(fl), None) == INVALID
+    assert lib.gqa_peak_mfma_bf16(P, 1, None, ctypes.byref(fl), None) == INVALID
+    assert lib.gqa_peak_mfma_bf16(P, 1, P, None, None) == INVALID
+    assert lib.gqa_peak_mfma_bf16(P + 4, 1, P, ctypes.byref(fl), None) == INVALID
+
+
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is visible: would launch")
 def test_valid_calls_report_no_device():
     assert _prefill() == NO_DEVICE
@@ -224,6 +239,8 @@ def test_valid_calls_report_no_device():
     assert _gqe() == NO_DEVICE
     assert _gqe_decode() == NO_DEVICE
     assert _build() == NO_DEVICE
+    assert lib.gqa_peak_hbm_read(P, 16, P, None) == NO_DEVICE
+    assert lib.gqa_peak_mfma_bf16(P, 1, P, ctypes.byref(ctypes.c_double(0.0)), None) == NO_DEVICE
 
 
 def test_kv_cache_bytes_matches_oracle_law():
