@@ -44,11 +44,20 @@ gqa_status check_prefill_shape(const void* q, const void* k, const void* v, cons
   if (!q || !k || !v || !out) return fail(GQA_ERR_INVALID_ARG, "null tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(GQA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-  if (in_dt == GQA_BF16 && !gqa::attn_bf16_supports(d))
-    return fail(GQA_ERR_UNSUPPORTED, "bf16 prefill supports d in {64, 128}, got %d", d);
+  if (in_dt == GQA_BF16 && !gqa::attn_bf16_supports(d) && d != 16 && d != 32)
+    return fail(GQA_ERR_UNSUPPORTED, "bf16 prefill supports d in {16, 32, 64, 128}, got %d", d);
   if (in_dt == GQA_F32 && !gqa::attn_f32_supports(d))
     return fail(GQA_ERR_UNSUPPORTED, "fp32 prefill supports d in {16, 32, 64, 128}, got %d", d);
   return GQA_OK;
+}
+
+// bf16 inputs run on the MFMA kernel where its tiles fit the head dim (64,
+// 128), else (16, 32) on the fp32-arithmetic kernel; fp32 inputs always on
+// the latter.
+hipError_t launch_prefill(gqa::AttnParams& p, gqa_dtype in_dtype, hipStream_t st) {
+  if (in_dtype == GQA_BF16 && gqa::attn_bf16_supports(p.d)) return gqa::launch_attn_bf16(p, st);
+  p.in_bf16 = in_dtype == GQA_BF16;
+  return gqa::launch_attn_f32(p, st);
 }
 
 gqa_status check_device() {
@@ -162,8 +171,7 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, void* out, i
   p.causal = causal;
   p.out_bf16 = out_dtype == GQA_BF16;
   auto st = static_cast<hipStream_t>(stream);
-  const hipError_t e = in_dtype == GQA_BF16 ? gqa::launch_attn_bf16(p, st) : gqa::launch_attn_f32(p, st);
-  return hip_status(e, "gqa_prefill launch");
+  return hip_status(launch_prefill(p, in_dtype, st), "gqa_prefill launch");
 }
 
 size_t gqa_decode_workspace_bytes(int B, int h, int g, int T_max, int d) {
@@ -304,7 +312,8 @@ gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v, const
     return fail(GQA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   if ((s = check_device()) != GQA_OK) return s;
   // Key splitting (bf16 causal launches only) needs the workspace.
-  const size_t need = in_dtype == GQA_BF16 ? gqa::attn_bf16_split_ws_bytes(B, g, T, d, top_k, causal) : 0;
+  const size_t need = in_dtype == GQA_BF16 && gqa::attn_bf16_supports(d)
+                          ? gqa::attn_bf16_split_ws_bytes(B, g, T, d, top_k, causal) : 0;
   if (workspace && workspace_bytes < need)
     return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   auto st = static_cast<hipStream_t>(stream);
@@ -321,8 +330,7 @@ gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v, const
   p.out_bf16 = out_dtype == GQA_BF16;
   p.zero_unselected = 1;
   p.split_ws = need > 0 ? workspace : nullptr;
-  const hipError_t e = in_dtype == GQA_BF16 ? gqa::launch_attn_bf16(p, st) : gqa::launch_attn_f32(p, st);
-  return hip_status(e, "gqe routed attention launch");
+  return hip_status(launch_prefill(p, in_dtype, st), "gqe routed attention launch");
 }
 
 gqa_status gqa_peak_hbm_read(const void* buf, size_t bytes, uint32_t* xor_out, void* stream) {

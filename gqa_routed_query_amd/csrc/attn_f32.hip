@@ -1,5 +1,7 @@
-// Grouped-query attention prefill with fp32 inputs and fp32 arithmetic
-// throughout (no bf16 anywhere), for dense GQA and routed GQE rows.
+// Grouped-query attention prefill in fp32 arithmetic throughout, for dense
+// GQA and routed GQE rows: fp32 inputs (no bf16 anywhere), and bf16 inputs at
+// the head dims below the bf16 MFMA kernel's tiles (16 and 32), upcast exactly
+// to fp32 as they are loaded.
 //
 // Same definition as the bf16 kernel (ml-canon "56 GQA / MQA", PyTorch GQA
 // function; IBM Think GQA page, scaled dot-product attention; causal mask
@@ -21,9 +23,9 @@ constexpr int kThreads = 256;
 constexpr int kBNF = 32;  // keys per tile
 
 struct KArgs {
-  const float* q;
-  const float* k;
-  const float* v;
+  const void* q;  // fp32, or bf16 when the kernel's IN_BF16 is set
+  const void* k;
+  const void* v;
   void* out;
   const int32_t* idx;
   const float* gate;
@@ -61,7 +63,26 @@ __device__ void zero_unselected_rows_f32(const KArgs& a, int b, int gam, int row
   }
 }
 
-template <int D, bool ROUTED>
+// Element i of an fp32 or bf16 array, as fp32 (bf16 widens exactly).
+template <bool IN_BF16>
+__device__ __forceinline__ float load_elt(const void* base, size_t i) {
+  if constexpr (IN_BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[i]);
+  else return static_cast<const float*>(base)[i];
+}
+
+// Four consecutive elements starting at i (a multiple of 4), as fp32.
+template <bool IN_BF16>
+__device__ __forceinline__ float4 load_4(const void* base, size_t i) {
+  if constexpr (IN_BF16) {
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + i);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+  } else {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + i);
+  }
+}
+
+template <int D, bool ROUTED, bool IN_BF16>
 __global__ __launch_bounds__(kThreads) void attn_f32_kernel(KArgs a) {
   constexpr int EPL = D < 32 ? D : 32;  // elements per lane
   constexpr int LPR = D / EPL;          // lanes per row (1, 2 or 4)
@@ -101,16 +122,15 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(KArgs a) {
 
   float qv[EPL], acc[EPL];
   {
-    const float* qrow = a.q + ((size_t)(b * a.h + head) * a.T + t_row) * D + part * EPL;
+    const size_t q0 = ((size_t)(b * a.h + head) * a.T + t_row) * D + part * EPL;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      qv[e] = qrow[e];
+      qv[e] = load_elt<IN_BF16>(a.q, q0 + e);
       acc[e] = 0.0f;
     }
   }
   float m_run = -INFINITY, l_run = 0.0f;
-  const float* kbase = a.k + (size_t)bg * a.T * D;
-  const float* vbase = a.v + (size_t)bg * a.T * D;
+  const size_t kv0 = (size_t)bg * a.T * D;
 
   for (int key0 = 0; key0 < n_keys; key0 += kBNF) {
     __syncthreads();
@@ -120,8 +140,8 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(KArgs a) {
       const int key = key0 + row;
       float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
       if (key < a.T) {
-        kk = *reinterpret_cast<const float4*>(kbase + (size_t)key * D + col);
-        vv = *reinterpret_cast<const float4*>(vbase + (size_t)key * D + col);
+        kk = load_4<IN_BF16>(a.k, kv0 + (size_t)key * D + col);
+        vv = load_4<IN_BF16>(a.v, kv0 + (size_t)key * D + col);
       }
       *reinterpret_cast<float4*>(Ks + row * D + col) = kk;
       *reinterpret_cast<float4*>(Vs + row * D + col) = vv;
@@ -181,9 +201,9 @@ hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
   constexpr int EPL = D < 32 ? D : 32;
   constexpr int RPB = kThreads / (D / EPL);
   KArgs a;
-  a.q = static_cast<const float*>(p.q);
-  a.k = static_cast<const float*>(p.k);
-  a.v = static_cast<const float*>(p.v);
+  a.q = p.q;
+  a.k = p.k;
+  a.v = p.v;
   a.out = p.out;
   a.idx = p.idx;
   a.gate = p.gate;
@@ -200,10 +220,17 @@ hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
   a.out_bf16 = p.out_bf16;
   a.zero_unselected = p.zero_unselected;
   const dim3 grid(a.n_row_tiles * a.BG), block(kThreads);
-  if (p.idx)
-    hipLaunchKernelGGL((attn_f32_kernel<D, true>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_f32_kernel<D, false>), grid, block, 0, stream, a);
+  if (p.in_bf16) {
+    if (p.idx)
+      hipLaunchKernelGGL((attn_f32_kernel<D, true, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_f32_kernel<D, false, true>), grid, block, 0, stream, a);
+  } else {
+    if (p.idx)
+      hipLaunchKernelGGL((attn_f32_kernel<D, true, false>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_f32_kernel<D, false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -214,6 +241,7 @@ bool attn_f32_supports(int d) { return d == 16 || d == 32 || d == 64 || d == 128
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream) {
   if (p.out_slots || p.q_b || p.kv_b || p.o_b || p.o_h || p.o_t || p.q_shared)
     return hipErrorInvalidValue;  // default layout only
+  if (p.in_bf16 && p.d > 32) return hipErrorInvalidValue;  // bf16 at d >= 64 runs on the MFMA kernel
   switch (p.d) {
     case 16: return launch_d<16>(p, stream);
     case 32: return launch_d<32>(p, stream);

@@ -26,6 +26,7 @@ struct AttnParams {
   float scale;          // > 0
   int causal;           // 0 or 1
   int out_bf16;         // 1: bf16 output, 0: fp32 output
+  int in_bf16;          // fp32-arithmetic kernel only: 1 when q, k, v are bf16 (d 16 or 32)
   int zero_unselected;  // routed only: write zeros to the rows of unselected heads
   // Layout overrides (bf16 kernel only; 0 keeps the [B,h,T,d] / [B,g,T,d] default):
   int out_slots;        // routed: row (t, gam, j) goes to output slot gam*R + j, ungated
@@ -96,7 +97,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_peak_hbm_read(const void* buf, size_t bytes, unsigned* x_out, hipStream_t stream);
 hipError_t launch_peak_mfma_bf16(const void* operands, int iters, float* sum_out, double* flops, hipStream_t stream);
 
-// Head dims with a bf16 MFMA prefill kernel / an fp32 kernel / a decode kernel.
+// Head dims with a bf16 MFMA prefill kernel / an fp32-arithmetic kernel (fp32
+// inputs at every listed d, bf16 inputs at d 16 and 32) / a decode kernel.
 bool attn_bf16_supports(int d);
 // Workspace bytes a routed causal bf16 launch of this shape may use for key splits
 // (0 when it would split nothing); R is the number of rows per token.

@@ -75,8 +75,10 @@ int gqa_abi_version(void);
  *   out [B, h, T, d] out_dtype (written in full)
  * out[b, i, t] = sum_j softmax_j(scale * q[b,i,t] . k[b, i/(h/g), j]) v[b, i/(h/g), j]
  * over j <= t when causal, over all j < T otherwise.
- * Supported: in_dtype BF16 with d in {64, 128}; in_dtype F32 with
- * d in {16, 32, 64, 128}; out_dtype F32 or BF16 (round to nearest even).
+ * Supported: d in {16, 32, 64, 128} for both input dtypes; out_dtype F32 or
+ * BF16 (round to nearest even). bf16 inputs at d 64 and 128 run on the matrix
+ * cores (P rounded to bf16 for the P.V product, fp32 accumulation); fp32
+ * inputs, and bf16 inputs at d 16 and 32, run in fp32 arithmetic throughout.
  */
 gqa_status gqa_prefill(const void* q, const void* k, const void* v, void* out,
                        int B, int h, int g, int T, int d,

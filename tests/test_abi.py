@@ -64,7 +64,8 @@ def _prefill(**kw):
     (dict(out=P + 4), INVALID),            # misaligned
     (dict(i=7), INVALID),                  # unknown dtype
     (dict(d=48), UNSUPPORTED),
-    (dict(i=BF16, d=16), UNSUPPORTED),
+    (dict(i=BF16, d=48), UNSUPPORTED),     # bf16: d in {16, 32, 64, 128}
+    (dict(i=BF16, d=8), UNSUPPORTED),
     (dict(h=1 << 20, g=1, T=1 << 12), INVALID),  # h*T beyond the row limit
 ])
 def test_prefill_rejects(kw, status):

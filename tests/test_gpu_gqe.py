@@ -31,6 +31,8 @@ def _run(q, k, v, lg, top_k, causal=True, out_dtype=torch.float32, workspace=Tru
     (1, 32, 1, 80, 128, 5, False, "bf16"),   # one group of 32 experts
     (1, 4, 2, 40, 16, 1, False, "f32"),
     (1, 8, 2, 70, 32, 2, True, "f32"),
+    (2, 8, 2, 90, 16, 1, False, "bf16"),    # bf16 below the MFMA tiles: fp32 arithmetic
+    (1, 8, 4, 150, 32, 2, True, "bf16"),
 ])
 def test_gqe_shapes(B, h, g, T, d, top_k, ties, dt):
     say(f"gqe B={B} h={h} g={g} T={T} d={d} k={top_k} ties={ties} {dt}")

@@ -70,6 +70,22 @@ def test_bf16_shapes(B, h, g, T, d, causal, out_dt):
     assert err <= TOL_BF16, err
 
 
+@pytest.mark.parametrize("B,h,g,T,d,causal,out_dt", [
+    (2, 8, 2, 77, 16, True, torch.float32),
+    (1, 6, 3, 130, 32, False, torch.float32),
+    (1, 4, 1, 300, 32, True, torch.bfloat16),      # MQA, several key tiles, ragged tail
+    (1, 4, 4, 1, 16, True, torch.float32),         # T = 1
+])
+def test_bf16_small_head_dims(B, h, g, T, d, causal, out_dt):
+    """bf16 inputs at d 16 and 32 (below the MFMA kernel's tiles) run in fp32
+    arithmetic on the exact upcast inputs: fp32 tolerance for fp32 output."""
+    say(f"bf16 small d B={B} h={h} g={g} T={T} d={d} causal={causal} out={out_dt}")
+    q, k, v = prefill_inputs(B, h, g, T, d, "bf16", seed=250 + T + d)
+    out = _run(q, k, v, causal=causal, out_dtype=out_dt)
+    err = max_abs(out, oracle.gqa_ref(q, k, v, causal=causal))
+    assert err <= (TOL_F32 if out_dt == torch.float32 else TOL_BF16), err
+
+
 def test_bf16_explicit_scale():
     say("bf16 explicit scale 0.3")
     q, k, v = prefill_inputs(1, 8, 2, 150, 128, "bf16", seed=7)
