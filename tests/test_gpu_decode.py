@@ -83,6 +83,22 @@ def test_decode_split_invariance(monkeypatch):
         assert max_abs(o, ref) <= TOL_BF16
 
 
+def test_decode_one_long_stream_many_pieces(monkeypatch):
+    """One sequence of 40,000 keys on one KV head: with the default grid every
+    share holds 256 keys, so the stream is cut into 157 pieces and the merge
+    runs three rounds of 64 pieces; with 4 workgroups, 4 pieces."""
+    q, kc, vc, lens = decode_inputs(1, 8, 1, 40000, 128, (40000, 40000), seed=45)
+    ref = oracle.gqa_decode_ref(q, kc, vc, lens)
+    for units in (None, "4"):
+        if units:
+            monkeypatch.setenv("GQA_DECODE_UNITS", units)
+        else:
+            monkeypatch.delenv("GQA_DECODE_UNITS", raising=False)
+        say(f"decode one long stream, units={units}")
+        out = _run(q, kc, vc, lens)
+        assert max_abs(out, ref) <= TOL_BF16
+
+
 def test_decode_repeated_calls_reuse_workspace():
     """Back-to-back calls with different lengths on one workspace give the
     same result as fresh calls: partial slots are rewritten each call and
