@@ -28,8 +28,10 @@
  * Conventions for every entry point:
  *  - Memory: all tensor pointers are device pointers to caller-owned memory,
  *    contiguous row-major in the stated layouts, 16-byte aligned. The library
- *    allocates nothing and frees nothing; it keeps no state between calls
- *    except a thread-local error message.
+ *    allocates nothing and frees nothing. Between calls it keeps only a
+ *    thread-local error message and a host-side cache of the dispatch order
+ *    planned for each causal prefill shape (built once per shape under a
+ *    mutex, then read).
  *  - dtypes: GQA_F32 = IEEE fp32, GQA_BF16 = bfloat16 (raw 16-bit storage).
  *    Accumulation is always fp32; fp32 inputs are never rounded to bf16.
  *  - Execution: work is enqueued on `stream` (a hipStream_t, NULL = the
@@ -236,7 +238,9 @@ gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v,
  * a launch whose grid is less than two blocks per CU may split the key range
  * of its heaviest causal row tiles over two jobs whose partial results (the
  * row max, the row sum and the unnormalised output, fp32) are merged by a
- * second kernel: the same result, with the work spread over the chip.
+ * second kernel: the same result up to rounding (each part rounds its
+ * probabilities to bf16 against its own reference maximum), with the work
+ * spread over the chip.
  */
 size_t gqe_workspace_bytes(int B, int h, int g, int T, int d, int top_k);
 
