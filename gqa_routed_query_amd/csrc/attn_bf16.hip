@@ -142,13 +142,13 @@ __device__ void zero_unselected_rows(const KArgs& a, int b, int gam, int row0, i
     for (int j = 0; j < R; ++j) kept |= (sel[j] == head);
     if (kept) continue;
     const size_t off = b * a.o_b + head * a.o_h + t * a.o_t + ch * 8;
-    const uint4 z = {0u, 0u, 0u, 0u};
+    const u32x4 z = {0u, 0u, 0u, 0u};
     if (a.out_bf16) {
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + off) = z;
+      __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + off));
     } else {
-      uint4* p = reinterpret_cast<uint4*>(static_cast<float*>(a.out) + off);
-      p[0] = z;
-      p[1] = z;
+      u32x4* p = reinterpret_cast<u32x4*>(static_cast<float*>(a.out) + off);
+      __builtin_nontemporal_store(z, p);
+      __builtin_nontemporal_store(z, p + 1);
     }
   }
 }
@@ -481,7 +481,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
         const size_t orow = shared ? ((size_t)b * a.T + ri.x) * D : b * a.o_b + oslot * a.o_h + ri.x * a.o_t;
         char* const outp = static_cast<char*>(shared ? a.out_sh : a.out);
         const size_t ob = orow * (a.out_bf16 ? 2 : 4) + (size_t)pass * D * 2 + gran * 16;
-        *reinterpret_cast<u32x4*>(outp + ob) = v;
+        // Nontemporal: the output is not read again here, and streaming it
+        // past L2 leaves the K/V tiles that other row tiles reuse in place.
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(outp + ob));
       }
     }
     if (pass + 1 < n_pass) __syncthreads();
@@ -536,12 +538,15 @@ __global__ __launch_bounds__(256) void split_merge_kernel(KArgs a) {
     const int oslot = a.out_slots ? gam * a.R + slot : head;
     const size_t off = b * a.o_b + oslot * a.o_h + t * a.o_t + ch * 8;
     if (a.out_bf16) {
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + off) = make_uint4(
-          pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+      const u32x4 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7])};
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + off));
     } else {
-      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.out) + off);
-      dst[0] = make_float4(v[0], v[1], v[2], v[3]);
-      dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<float*>(a.out) + off);
+      __builtin_nontemporal_store(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                        __float_as_uint(v[3])}, dst);
+      __builtin_nontemporal_store(u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                                        __float_as_uint(v[7])}, dst + 1);
     }
   }
 }
