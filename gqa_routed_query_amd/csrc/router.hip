@@ -113,9 +113,11 @@ __global__ __launch_bounds__(kPW * 64) void router_proj_kernel(ProjArgs a) {
       const int col = q * 8 < width ? q * 8 : 0;
       const uint16_t* src = tl == 0 ? a.x + (size_t)min(tok0 + r, a.n_tok - 1) * a.dm
                                     : a.w + (size_t)min((tl - 1) * 32 + r, a.h - 1) * a.dm;
-      __builtin_amdgcn_global_load_lds(src + c0 + col,
-                                       (__attribute__((address_space(3))) void*)(Xb + tl * kTileEl + (i % 16) * 2 * kRowEl),
-                                       16, 0, 0);
+      auto* const dst = (__attribute__((address_space(3))) void*)(Xb + tl * kTileEl + (i % 16) * 2 * kRowEl);
+      if (tl == 0)  // x is read once: nontemporal
+        __builtin_amdgcn_global_load_lds(src + c0 + col, dst, 16, 0, 2);
+      else          // W_r is read by every workgroup
+        __builtin_amdgcn_global_load_lds(src + c0 + col, dst, 16, 0, 0);
     }
   };
 
