@@ -1,10 +1,13 @@
 // Peak microbenchmarks (measurement support): the rates the path's kernels
 // are compared with besides the datasheet peaks of MI355X.
-//  * An HBM read stream: every 16-byte word of a buffer read once, each
-//    workgroup streaming a contiguous chunk with eight 16-byte loads in
-//    flight per lane. The XOR of all words
-//    comes back (one atomic per workgroup), so a test can check that every
-//    word was read exactly once.
+//  * An HBM read stream: every 16-byte word of a buffer read once, two
+//    4-wave workgroups per CU (the decode kernel's grid), each streaming a
+//    contiguous chunk with eight 16-byte loads in flight per lane. The XOR of
+//    all words comes back (one atomic per workgroup), so a test can check that
+//    every word was read exactly once. The workgroups finish together, so
+//    their atomics on the one result word queue up at the end of the launch:
+//    with eight workgroups per CU that queue cost about 10% of a 4 GiB read,
+//    with two it is a few microseconds.
 //  * An MFMA-only loop: v_mfma_f32_32x32x16_bf16 on register operands, four
 //    independent accumulators per wave and two waves per SIMD on every SIMD
 //    of the chip. The sum of all accumulators comes back (one atomic per
@@ -29,15 +32,20 @@ __global__ __launch_bounds__(kPeakThreads) void hbm_read_kernel(const u32x4* buf
   const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
   const size_t lo = min((size_t)blockIdx.x * per, n16), hi = min(lo + per, n16);
   u32x4 acc = {0u, 0u, 0u, 0u};
-  size_t i = lo + threadIdx.x;
-  for (; i + (kReadUnroll - 1) * kPeakThreads < hi; i += kStep) {
+  const u32x4* const chunk = buf + lo;
+  const size_t n = hi - lo;
+  size_t i = threadIdx.x;
+  for (; i + (kReadUnroll - 1) * kPeakThreads < n; i += kStep) {
     u32x4 w[kReadUnroll];
 #pragma unroll
-    for (int k = 0; k < kReadUnroll; ++k) w[k] = __builtin_nontemporal_load(buf + i + k * kPeakThreads);
+    for (int k = 0; k < kReadUnroll; ++k) w[k] = __builtin_nontemporal_load(chunk + i + k * kPeakThreads);
+    // Keep the scheduler from pulling the first XOR (and its wait) in between
+    // the loads, which would leave two of them in flight instead of eight.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < kReadUnroll; ++k) acc ^= w[k];
   }
-  for (; i < hi; i += kPeakThreads) acc ^= buf[i];
+  for (; i < n; i += kPeakThreads) acc ^= chunk[i];
   unsigned x = acc.x ^ acc.y ^ acc.z ^ acc.w;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x ^= __shfl_xor(x, o);
@@ -91,7 +99,7 @@ int device_cu_count() {
 }  // namespace
 
 hipError_t launch_peak_hbm_read(const void* buf, size_t bytes, unsigned* x_out, hipStream_t stream) {
-  const dim3 grid(device_cu_count() * 8), block(kPeakThreads);
+  const dim3 grid(device_cu_count() * 2), block(kPeakThreads);
   hipLaunchKernelGGL(hbm_read_kernel, grid, block, 0, stream, static_cast<const u32x4*>(buf), bytes / 16, x_out);
   return hipGetLastError();
 }
