@@ -126,12 +126,17 @@ def test_gqe_workspace_bytes():
     """Key splitting is planned only for causal grids of less than two blocks
     per CU, upper-half row tiles only: the GQE workload (B=2, T=4096, h=32, g=8,
     k=1) needs a workspace, large grids need none, invalid shapes return 0.
-    Without a GPU the size is computed for 256 CUs (MI355X)."""
+    Without a GPU the size is computed for 256 CUs (MI355X). At k=1 the split
+    launch takes the 12-wave grid (384-row tiles: 11 per problem, at most 5 in
+    the upper half with a split point)."""
     small = gq.gqe_workspace_bytes(2, 32, 8, 4096, 128, 1)
     assert small > 0 and small % 16 == 0
     # one split row tile holds its two partial results: 2 * rows * (d + 2) floats per problem
-    per_tile = 2 * 2 * 8 * 256 * (128 + 2) * 4
-    assert small % per_tile == 0 and small // per_tile <= 8
+    per_tile = 2 * 2 * 8 * 384 * (128 + 2) * 4
+    assert small % per_tile == 0 and small // per_tile <= 6
+    # at k=2 the grid takes two rounds of 12-wave blocks: the 8-wave grid (256-row tiles) is split
+    k2 = gq.gqe_workspace_bytes(2, 32, 8, 4096, 128, 2)
+    assert k2 == 0 or k2 % (2 * 2 * 8 * 256 * (128 + 2) * 4) == 0
     assert gq.gqe_workspace_bytes(64, 32, 8, 4096, 128, 1) == 0   # 2048+ blocks: no split
     assert gq.gqe_workspace_bytes(2, 32, 8, 4096, 128, 5) == 0    # top_k > h/g
     assert gq.gqe_workspace_bytes(2, 32, 8, 4096, 96, 1) == 0     # d not run on the bf16 kernel

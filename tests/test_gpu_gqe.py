@@ -143,7 +143,10 @@ def test_gqe_key_split_matches_unsplit(B, h, g, T, d, top_k, out_dt):
     b, ib, gb = gq.gqe_routed_prefill(q, k, v, lg, top_k, out_dtype=out_dt, workspace=None)
     torch.cuda.synchronize()
     assert torch.equal(ia, ib) and torch.equal(ga, gb)
-    assert torch.equal(a == 0, b == 0)
+    # The same rows are all zero (the heads the router did not keep). Single
+    # elements of a kept row may sum to exactly 0.0 in one order of additions
+    # and not in the other, so the check is per row.
+    assert torch.equal((a == 0).all(-1), (b == 0).all(-1))
     # The probabilities are rounded to bf16 against each part's own reference
     # max, so the two launches differ at bf16 precision even with fp32 output.
     assert max_abs(a, b) <= TOL_BF16, max_abs(a, b)
