@@ -21,7 +21,9 @@
 //    waves per SIMD, which hides more of those latencies than larger tiles at
 //    two waves per SIMD. Grids too small to give every CU two such workgroups
 //    (short routed problems) use 8 waves with 64-key tiles instead, halving the
-//    per-tile overhead and spreading the rows over more workgroups.
+//    per-tile overhead and spreading the rows over more workgroups, unless key
+//    splitting (below) makes a grid of at most one 12-wave block per CU run as
+//    one round.
 //    Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16 so that each lane ends up owning one query row
 //    (column l%32); the probabilities are then already in the B-operand layout
