@@ -513,10 +513,27 @@ def cpu_baseline(pq, pk, pv, wp):
     out = oracle.gqa_ref(q, k, v, causal=True)
     dt = time.perf_counter() - t0
     assert np.isfinite(out).all()
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = None
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "seconds": dt,
+            "seconds": dt, "blas_threads": threads, "cpu_count": os.cpu_count(),
+            "sched_affinity": affinity, "cpu_model": cpu_model(),
             "sample": "float64 oracle, whole prefill workload B=4 h=32 g=8 T=2048 d=128 causal "
                       f"({flops/1e9:.2f} GFLOP algorithmic); host cpu_count={os.cpu_count()}"}
+
+
+def cpu_model():
+    """The host CPU's model string (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
 
 
 if __name__ == "__main__":
