@@ -137,6 +137,11 @@ def test_gqe_workspace_bytes():
     # at k=2 the grid takes two rounds of 12-wave blocks: the 8-wave grid (256-row tiles) is split
     k2 = gq.gqe_workspace_bytes(2, 32, 8, 4096, 128, 2)
     assert k2 == 0 or k2 % (2 * 2 * 8 * 256 * (128 + 2) * 4) == 0
+    # small split grids keep 12 waves too: B=2, g=2, T=300, k=2 is 600 rows per problem, two
+    # 384-row tiles (one in the upper half); B=1, g=4, T=333, d=64, k=3 is 999 rows, three tiles
+    assert gq.gqe_workspace_bytes(2, 8, 2, 300, 128, 2) == 1 * (2 * 2) * 2 * 384 * (128 + 2) * 4
+    w = gq.gqe_workspace_bytes(1, 12, 4, 333, 64, 3)
+    assert w > 0 and w % ((1 * 4) * 2 * 384 * (64 + 2) * 4) == 0
     assert gq.gqe_workspace_bytes(64, 32, 8, 4096, 128, 1) == 0   # 2048+ blocks: no split
     assert gq.gqe_workspace_bytes(2, 32, 8, 4096, 128, 5) == 0    # top_k > h/g
     assert gq.gqe_workspace_bytes(2, 32, 8, 4096, 96, 1) == 0     # d not run on the bf16 kernel
