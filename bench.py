@@ -9,16 +9,19 @@ One step runs the whole path once on resident synthetic inputs:
   * GQE routed causal prefill, bf16: B=2, T=4096, h=32, g=8, d=128, top-k 1
     and 2 (TFLOP/s of the kept rows).
 Every kernel call is bracketed by HIP events recorded on the stream the
-library launches on (torch's current stream). Before each decode call a
+library launches on (torch's current stream). Before every timed call a
 1 GiB buffer is read (outside the events) so the 256 MB Infinity Cache and
-the L2s hold none of the KV cache; a read is used rather than a write so that
-no dirty lines are written back during the timed call. Work is counted algorithmically: causal prefill
-flops are 4*d per visible (query, key) pair, GQE flops only for kept rows,
-decode bytes only for cached positions below lens[b] (plus q and out).
+the L2s hold none of the call's inputs; a read is used rather than a write so
+that no dirty lines are written back during the timed call. Work is counted
+algorithmically: causal prefill flops are 4*d per visible (query, key) pair,
+GQE flops only for kept rows, decode bytes only for cached positions below
+lens[b] (plus q and out).
 
 After the timed steps, the KV-group sweep (decode, B=32, T=16384, g in
-{1, 4, 8, 32}) is timed the same way, and the float64 CPU oracle is timed on
-a bounded sample of the prefill workload (cpu_baseline).
+{1, 4, 8, 32}) is timed the same way, with the HBM bytes the counters measured
+per g (profiles/traffic_counters.json) beside the cache-size law, and the
+float64 CPU oracle is timed on the whole prefill workload (cpu_baseline); its
+output is compared with the GPU's, element by element.
 
 Prints ONE JSON line. Only one GPU is supported.
 """
@@ -58,8 +61,9 @@ def parse():
                     help="skip the peak microbenchmarks (HBM read stream, MFMA-only loop)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the sweeps outside the step (KV-group decode, GQE vs GQA over T)")
-    ap.add_argument("--only", choices=["prefill", "decode", "gqe", "copy"], default=None,
-                    help="profile helper: run only one kernel family (copy = calibration copy)")
+    ap.add_argument("--only", choices=["prefill", "decode", "gqe", "sweep", "copy"], default=None,
+                    help="profile helper: run only one kernel family (sweep = the KV-group decode "
+                         "sweep, two calls per g; copy = calibration copy)")
     return ap.parse_args()
 
 
@@ -68,7 +72,7 @@ def source_hash(rel):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_for(name, n_launch_units=1):
+def traffic_for(name, field="bytes_per_launch"):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source; else None."""
     try:
@@ -76,9 +80,10 @@ def traffic_for(name, n_launch_units=1):
             rec = json.load(f)[name]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[name]):
+    src = rec.get("source", KERNEL_SOURCES.get(name))
+    if not src or rec.get("source_sha256_16") != source_hash(src):
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get(field)
 
 
 class Timer:
@@ -121,7 +126,7 @@ def main():
     log(f"device {torch.cuda.get_device_name(dev)}, lib {gq.lib_path}")
 
     wp, wd, wg = WORKLOADS["prefill"], WORKLOADS["decode"], WORKLOADS["gqe"]
-    # Cache eviction between decode calls: READ 1 GiB (a write would leave
+    # Cache eviction before every timed call: READ 1 GiB (a write would leave
     # dirty lines whose write-back competes with the timed kernel).
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
 
@@ -138,6 +143,7 @@ def main():
     run_prefill = args.only in (None, "prefill")
     run_decode = args.only in (None, "decode")
     run_gqe = args.only in (None, "gqe")
+    run_sweep = args.only == "sweep" or (args.only is None and not args.no_sweep)
 
     # ---- inputs, resident in HBM before any timing ----
     if run_prefill:
@@ -167,7 +173,9 @@ def main():
     t_gqa_same = Timer(torch)  # dense GQA at the GQE shape, for the speedup ratio
 
     def step(timed):
+        # every call starts with no input in the Infinity Cache or the L2s
         if run_prefill:
+            flush.sum()
             with (t_pre if timed else Timer(torch)):
                 gq.gqa_prefill(pq, pk, pv, causal=True, out=pout)
         if run_decode:
@@ -176,9 +184,11 @@ def main():
                 gq.gqa_decode(dq, dk, dv, dlens, out=dout, workspace=dws)
         if run_gqe:
             for kk in wg.top_k:
+                flush.sum()
                 with (t_gqe[kk] if timed else Timer(torch)):
                     gq.gqe_routed_prefill(gq_, gk, gv, glg, kk, causal=True, out=gout,
                                           workspace=gws[kk])
+            flush.sum()
             with (t_gqa_same if timed else Timer(torch)):
                 gq.gqa_prefill(gq_, gk, gv, causal=True, out=gout)
 
@@ -226,7 +236,7 @@ def main():
 
     # ---- GQE routed decode at the decode workload, outside the step ----
     gdec = {}
-    if run_decode and not args.no_sweep:
+    if run_decode and run_sweep:
         dlg = router_logits(wd.B, 1, wd.h, seed=wd.seed + 100, device=dev)[:, 0].contiguous()
         for kk in (1, 2):
             tm = Timer(torch)
@@ -251,9 +261,13 @@ def main():
 
     # ---- KV-group sweep (decode), outside the step ----
     sweep = []
-    if run_decode and not args.no_sweep:
-        del dk, dv
+    if (run_decode or args.only == "sweep") and run_sweep:
+        if run_decode:
+            del dk, dv
         ws = WORKLOADS["decode_sweep"]
+        # profile runs (--only sweep) make two calls per g, in the order of g_sweep
+        n_warm, n_time = (1, 1) if args.only == "sweep" else (3, 10)
+        kv_mha = gq.gqa_kv_cache_bytes(ws.B, ws.h, ws.T, ws.d)
         for g in ws.g_sweep:
             q, kc, vc, lens = decode_inputs(ws.B, ws.h, g, ws.T, ws.d, ws.lens, seed=ws.seed + g,
                                             device=dev)
@@ -261,19 +275,25 @@ def main():
             wsb = torch.empty(max(gq.gqa_decode_workspace_bytes(ws.B, ws.h, g, ws.T, ws.d), 1),
                               dtype=torch.uint8, device=dev)
             tm = Timer(torch)
-            for it in range(3 + 10):
+            for it in range(n_warm + n_time):
                 flush.sum()
-                if it < 3:
+                if it < n_warm:
                     gq.gqa_decode(q, kc, vc, lens, out=out, workspace=wsb)
                     continue
                 with tm:
                     gq.gqa_decode(q, kc, vc, lens, out=out, workspace=wsb)
             torch.cuda.synchronize()
             st = stats(tm.ms())
+            # the cache-size law 2 * n_kv * d * T * sizeof(bf16) * B, and the HBM
+            # bytes the counters measured for one call (null when they were
+            # taken on another kernel source)
             kv = gq.gqa_kv_cache_bytes(ws.B, g, ws.T, ws.d)
             nbytes = kv + 2 * q.numel() * 2
+            measured = traffic_for(f"decode_sweep_g{g}", "fetch_bytes_per_launch")
             sweep.append(dict(g=g, heads_per_group=ws.h // g, kv_cache_bytes=kv,
-                              kv_bytes_over_2_nkv_d_T=kv / (2 * g * ws.d * ws.T),
+                              kv_cache_reduction_vs_mha=kv_mha / kv,
+                              measured_read_bytes=measured,
+                              measured_read_over_law=(measured / kv) if measured else None,
                               mean_ms=st["mean_ms"], GBps=nbytes / (st["mean_ms"] * 1e-3) / 1e9,
                               frac_peak=nbytes / (st["mean_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS))
             log(f"sweep g={g}: {st['mean_ms']*1e3:.1f} us, {sweep[-1]['GBps']:.0f} GB/s")
@@ -282,7 +302,7 @@ def main():
 
     # ---- GQE router with its projection (x W_r^T + top-k), outside the step ----
     grouter = {}
-    if run_gqe and not args.no_sweep:
+    if run_gqe and run_sweep:
         n_tok = wg.B * wg.T
         rx, rw = router_inputs(n_tok, ROUTER_D_MODEL, wg.h, seed=wg.seed + 200, device=dev)
         for kk in wg.top_k:
@@ -306,9 +326,7 @@ def main():
 
     # ---- GQE vs dense GQA over the sequence length, outside the step ----
     gsweep = []
-    if run_gqe and not args.no_sweep:
-        if run_prefill:
-            del pout
+    if run_gqe and run_sweep:
         del gq_, gk, gv, glg, gout, gws
         torch.cuda.empty_cache()
         for (B, h, g, T, d, ks, seed) in gqe_sweep_points():
@@ -319,6 +337,7 @@ def main():
             def timed(fn, n_warm=2, n=5):
                 tm = Timer(torch)
                 for it in range(n_warm + n):
+                    flush.sum()
                     if it < n_warm:
                         fn()
                         continue
@@ -359,10 +378,10 @@ def main():
     if args.only is None and not args.no_peaks:
         peaks = measured_peaks(torch, gq, dev)
 
-    # ---- CPU oracle baseline on a bounded sample of the prefill workload ----
+    # ---- CPU oracle baseline on the whole prefill workload, and its parity ----
     cpu = None
     if run_prefill and not args.no_cpu:
-        cpu = cpu_baseline(pq, pk, pv, wp)
+        cpu = cpu_baseline(pq, pk, pv, pout, wp)
 
     line = {
         "metric": METRIC,
@@ -493,10 +512,11 @@ def rocm_smi_clocks():
     return lines or None
 
 
-def cpu_baseline(pq, pk, pv, wp):
+def cpu_baseline(pq, pk, pv, pout, wp):
     """Time the float64 oracle on the whole prefill workload (B=4, h=32, g=8,
     T=2048, d=128, causal: 137.5 GFLOP of algorithmic work), on the same
-    inputs the GPU used."""
+    inputs the GPU used, then compare its output with the GPU's last timed
+    output element by element (outside the timed region)."""
     import numpy as np
 
     import oracle
@@ -512,7 +532,11 @@ def cpu_baseline(pq, pk, pv, wp):
     t0 = time.perf_counter()
     out = oracle.gqa_ref(q, k, v, causal=True)
     dt = time.perf_counter() - t0
-    assert np.isfinite(out).all()
+    gpu = pout.cpu().to(dtype=__import__("torch").float64).numpy()
+    err = float(np.abs(gpu - out).max())
+    tol = 2e-2  # bf16 inputs, fp32 accumulation
+    log(f"cpu baseline: {dt:.2f} s; GPU output vs oracle, all {out.size} elements: "
+        f"max|err| = {err:.3e} (tolerance {tol})")
     try:
         affinity = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
@@ -520,6 +544,8 @@ def cpu_baseline(pq, pk, pv, wp):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "seconds": dt, "blas_threads": threads, "cpu_count": os.cpu_count(),
             "sched_affinity": affinity, "cpu_model": cpu_model(),
+            "parity": {"max_abs_err": err, "tol": tol, "ok": err <= tol, "elements": int(out.size),
+                       "compared": "GPU bf16 output of the timed prefill launch vs the float64 oracle"},
             "sample": "float64 oracle, whole prefill workload B=4 h=32 g=8 T=2048 d=128 causal "
                       f"({flops/1e9:.2f} GFLOP algorithmic); host cpu_count={os.cpu_count()}"}
 

@@ -31,7 +31,7 @@ def hipcc() -> str:
 
 
 def build_command(out: str = LIB_PATH) -> list[str]:
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -175,7 +175,7 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, void* out, i
 }
 
 size_t gqa_decode_workspace_bytes(int B, int h, int g, int T_max, int d) {
-  if (B <= 0 || h < 1 || g < 1 || h % g || T_max <= 0 || d <= 0) return 0;
+  if (B < 0 || h < 1 || g < 1 || h % g || T_max < 0 || d <= 0) return 0;
   return decode_layout(h, g, d).total;
 }
 

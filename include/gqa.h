@@ -57,16 +57,30 @@
 extern "C" {
 #endif
 
+/*
+ * Status codes and element types. Both are int-sized in every language; C++
+ * sees them with the fixed underlying type int, so any int a C caller passes
+ * (an unknown dtype, say) is a value of the type and is rejected by the
+ * argument checks rather than being undefined behaviour.
+ */
+#ifdef __cplusplus
+enum gqa_status : int {
+#else
 typedef enum {
+#endif
   GQA_OK = 0,
   GQA_ERR_INVALID_ARG = 1,
   GQA_ERR_UNSUPPORTED = 2,
   GQA_ERR_WORKSPACE = 3,
   GQA_ERR_NO_DEVICE = 4,
   GQA_ERR_HIP = 5
+#ifdef __cplusplus
+};
+enum gqa_dtype : int { GQA_F32 = 0, GQA_BF16 = 1 };
+#else
 } gqa_status;
-
 typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
+#endif
 
 /* Version of this ABI; bumped on any incompatible change. */
 int gqa_abi_version(void);
@@ -91,9 +105,10 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, void* out,
  * Bytes of device workspace gqa_decode needs: two partial results (h/g heads
  * of d fp32 values plus a max and a sum each) per wave of the decode grid,
  * which holds one wave per resident wave slot of the current device. It does
- * not depend on B or T_max (they are accepted for the shape check only);
- * 0 for an invalid shape. The GQA_DECODE_UNITS environment variable overrides
- * the wave count.
+ * not depend on B or T_max (they are accepted for the shape check only, and
+ * B = 0 or T_max = 0 give the same size as any other valid shape); 0 for an
+ * invalid shape. The GQA_DECODE_UNITS environment variable overrides the wave
+ * count.
  */
 size_t gqa_decode_workspace_bytes(int B, int h, int g, int T_max, int d);
 

@@ -265,12 +265,16 @@ def test_kv_cache_bytes_matches_oracle_law():
 
 
 def test_decode_workspace_bytes():
-    assert gq.gqa_decode_workspace_bytes(0, 8, 2, 100, 128) == 0
+    assert gq.gqa_decode_workspace_bytes(-1, 8, 2, 100, 128) == 0
+    assert gq.gqa_decode_workspace_bytes(2, 8, 2, -5, 128) == 0
     assert gq.gqa_decode_workspace_bytes(2, 8, 3, 100, 128) == 0   # g does not divide h
-    # two partials of r heads per wave of the grid: independent of B and T_max
+    # two partials of r heads per wave of the grid: independent of B and T_max,
+    # empty batches and empty caches included
     small = gq.gqa_decode_workspace_bytes(1, 8, 2, 100, 128)
     assert small > 0
     assert small == gq.gqa_decode_workspace_bytes(64, 8, 2, 16384, 128)
+    assert small == gq.gqa_decode_workspace_bytes(0, 8, 2, 100, 128)
+    assert small == gq.gqa_decode_workspace_bytes(3, 8, 2, 0, 128)
     # and proportional to r*(d+2) (up to the 256-byte alignment of the first region)
     r4 = gq.gqa_decode_workspace_bytes(64, 32, 8, 8192, 128)
     r1 = gq.gqa_decode_workspace_bytes(64, 32, 32, 8192, 128)
@@ -283,3 +287,16 @@ def test_decode_workspace_units_override(monkeypatch):
     monkeypatch.setenv("GQA_DECODE_UNITS", "3")
     # 3 waves x 2 partials x 4 heads x 128 floats (rounded to 256 B) + 3 x 2 x 4 x 2 floats
     assert gq.gqa_decode_workspace_bytes(4, 16, 4, 1000, 128) == 12288 + 192
+
+
+def test_decode_empty_cache_accepts_its_workspace():
+    """T_max = 0 (every row zero): the size query's workspace passes the
+    argument checks, so the call fails only for want of a device here. (With a
+    device it would launch on the stand-in pointers; the GPU tests cover it.)"""
+    if torch.cuda.is_available():
+        pytest.skip("a device is visible: the call would launch")
+    ws = gq.gqa_decode_workspace_bytes(2, 8, 2, 0, 128)
+    st = lib.gqa_decode(P, None, None, P, P, 2, 8, 2, 0, 128, BF16, BF16, 0.1, P, ws, None)
+    assert st == NO_DEVICE, gq.last_error()
+    st = lib.gqa_decode(P, None, None, P, P, 2, 8, 2, 0, 128, BF16, BF16, 0.1, P, ws - 1, None)
+    assert st == WORKSPACE

@@ -61,6 +61,22 @@ def test_decode_edge_lengths():
     assert max_abs(out, ref) <= TOL_BF16
 
 
+def test_decode_empty_cache():
+    """T_max = 0: no cached positions at all, every output row is zero, with the
+    workspace size the library reports for that shape."""
+    import gqa_routed_query_amd as gq
+
+    d = dev()
+    say("decode T_max = 0")
+    q = torch.randn(3, 8, 128, device=d).to(torch.bfloat16)
+    kc = torch.empty(3, 2, 0, 128, dtype=torch.bfloat16, device=d)
+    lens = torch.zeros(3, dtype=torch.int32, device=d)
+    ws = torch.empty(gq.gqa_decode_workspace_bytes(3, 8, 2, 0, 128), dtype=torch.uint8, device=d)
+    out = gq.gqa_decode(q, kc, kc, lens, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    assert float(out.abs().max()) == 0.0
+
+
 def test_decode_split_invariance(monkeypatch):
     """The result does not depend on how the key range is shared out over
     waves (up to fp32 rounding): one wave (every stream whole), a few waves
@@ -140,36 +156,41 @@ def test_decode_matches_prefill_last_row():
 
 def test_decode_headline_shape():
     """B=64, h=32, g=8, d=128, cache lengths uniform in [1024, 8192], cache
-    drawn on the GPU (seed 3); 8 sequences checked in full against the oracle,
-    the rest for finiteness."""
+    drawn on the GPU (seed 3), bf16 output as the benchmark launches it: every
+    sequence against the oracle, one at a time (its valid cache positions only)."""
     w = WORKLOADS["decode"]
     d = dev()
-    say("decode headline shape")
+    say("decode headline shape, all sequences")
     q, kc, vc, lens = decode_inputs(w.B, w.h, w.g, w.T, w.d, w.lens, seed=w.seed, device=d)
-    out = _run(q, kc, vc, lens)
-    assert torch.isfinite(out).all()
+    out = _run(q, kc, vc, lens, out_dtype=torch.bfloat16)
     lens_c = lens.cpu()
-    picks = sorted({int(lens_c.argmin()), int(lens_c.argmax()), 0, 1, 17, 33, 50, 63})
-    for b in picks:
+    oc = out.cpu()
+    worst = 0.0
+    for b in range(w.B):
         n = int(lens_c[b])
         ref = oracle.gqa_decode_ref(q[b:b + 1].cpu(), kc[b:b + 1, :, :n].cpu(),
                                     vc[b:b + 1, :, :n].cpu(), np.array([n]))
-        assert max_abs(out[b:b + 1], ref) <= TOL_BF16, b
+        worst = max(worst, max_abs(oc[b:b + 1], ref))
+    assert worst <= TOL_BF16, worst
 
 
 @pytest.mark.parametrize("g", WORKLOADS["decode_sweep"].g_sweep)
 def test_decode_group_sweep(g):
-    """B=32, h=32, T=16384, d=128 at g in {1, 4, 8, 32}: two sequences checked
-    in full against the oracle, every output finite."""
+    """B=32, h=32, T=16384, d=128 at g in {1, 4, 8, 32}, bf16 output as the
+    benchmark launches it: all 32 sequences against the oracle, streamed one
+    sequence at a time."""
     w = WORKLOADS["decode_sweep"]
     d = dev()
-    say(f"decode sweep g={g}")
+    say(f"decode sweep g={g}, all sequences")
     q, kc, vc, lens = decode_inputs(w.B, w.h, g, w.T, w.d, w.lens, seed=w.seed + g, device=d)
-    out = _run(q, kc, vc, lens)
-    assert torch.isfinite(out).all()
-    for b in (0, w.B - 1):
+    out = _run(q, kc, vc, lens, out_dtype=torch.bfloat16)
+    oc = out.cpu()
+    worst = 0.0
+    for b in range(w.B):
         ref = oracle.gqa_decode_ref(q[b:b + 1].cpu(), kc[b:b + 1].cpu(), vc[b:b + 1].cpu(),
                                     np.array([w.T]))
-        assert max_abs(out[b:b + 1], ref) <= TOL_BF16, b
+        worst = max(worst, max_abs(oc[b:b + 1], ref))
+    say(f"decode sweep g={g}: max|err| {worst:.3e}")
+    assert worst <= TOL_BF16, worst
     del q, kc, vc
     torch.cuda.empty_cache()

@@ -115,8 +115,8 @@ def test_gqe_decode_kept_rows_equal_plain_decode():
 def test_gqe_decode_headline_shape(top_k):
     """The decode workload (B=64, h=32, g=8, d=128, cache lengths uniform in
     [1024, 8192], seed 3) with router logits [64, 32] ~ N(0,1): all indices
-    bit-exact and gates checked, every unselected row zero, 8 sequences in full
-    against the oracle."""
+    bit-exact and gates checked, every unselected row zero, every sequence in
+    full against the oracle (one at a time, its valid cache positions only)."""
     w = WORKLOADS["decode"]
     d = dev()
     say(f"gqe decode headline shape k={top_k}")
@@ -130,10 +130,10 @@ def test_gqe_decode_headline_shape(top_k):
     kept.scatter_(1, idx.view(w.B, -1).long(), True)
     assert torch.equal((out != 0).any(-1), kept)
     lens_c = lens.cpu()
-    picks = sorted({int(lens_c.argmin()), int(lens_c.argmax()), 0, 1, 17, 33, 50, 63})
-    for b in picks:
+    oc = out.cpu()
+    for b in range(w.B):
         n = int(lens_c[b])
         ref, _, _ = oracle.gqe_decode_ref(q[b:b + 1].cpu(), kc[b:b + 1, :, :n].cpu(),
                                           vc[b:b + 1, :, :n].cpu(), np.array([n]),
                                           lg[b:b + 1].cpu(), top_k)
-        assert max_abs(out[b:b + 1], ref) <= TOL_BF16, b
+        assert max_abs(oc[b:b + 1], ref) <= TOL_BF16, b
