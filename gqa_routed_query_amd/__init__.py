@@ -6,6 +6,8 @@ this package only marshals torch tensors into its entry points:
 
 * :func:`gqa_prefill` -- GQA prefill, q [B,h,T,d], k/v [B,g,T,d].
 * :func:`gqa_decode` -- one decode step over a KV cache [B,g,T_max,d].
+* :func:`gqa_decode_noalloc` -- the same step with the split partials in the
+  library's static device scratch, for callers that cannot allocate.
 * :func:`gqe_routed_prefill` -- GQE: top-k query-head experts per KV group
   per token, dense K/V.
 * :func:`gqe_routed_decode` -- GQE routing applied to one decode step.
@@ -26,6 +28,7 @@ from ._binding import (  # noqa: F401
     GqaError,
     abi_version,
     gqa_decode,
+    gqa_decode_noalloc,
     gqa_decode_workspace_bytes,
     gqa_kv_cache_bytes,
     gqa_prefill,

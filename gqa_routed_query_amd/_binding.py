@@ -47,6 +47,8 @@ def _load():
     lib.gqa_decode.restype = i32
     lib.gqa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                                vp, sz, vp]
+    lib.gqa_decode_noalloc.restype = i32
+    lib.gqa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
     lib.gqe_routed_prefill.restype = i32
     lib.gqe_routed_prefill.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32,
                                        i32, i32, i32, f32, i32, vp, sz, vp]
@@ -181,6 +183,31 @@ def gqa_decode(q, k_cache, v_cache, lens, scale: float | None = None, out=None,
                          scale, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                          _stream(dev))
     _check("gqa_decode", st)
+    return out
+
+
+def gqa_decode_noalloc(q, k_cache, v_cache, lens, out, scale: float | None = None):
+    """GQA decode with the split partials in the library's static device
+    scratch (the entry point allocates nothing; ``out`` [B,h,d] is the
+    caller's). Calls that overlap on one device race."""
+    dev = _dev(q, k_cache, v_cache, lens, out)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expected q [B,h,d] and caches [B,g,T_max,d]")
+    B, h, d = q.shape
+    if k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError("cache shape does not match q")
+    if lens.dtype != torch.int32 or lens.shape != (B,):
+        raise ValueError("lens must be int32 [B]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    if out.shape != q.shape:
+        raise ValueError("out must be [B,h,d]")
+    g, T_max = k_cache.shape[1], k_cache.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = _lib.gqa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lens.data_ptr(),
+                                 out.data_ptr(), B, h, g, T_max, d, _dt(q, "q"), _dt(out, "out"), scale,
+                                 _stream(dev))
+    _check("gqa_decode_noalloc", st)
     return out
 
 

@@ -90,13 +90,15 @@ DecodeLayout decode_layout(int h, int g, int d) {
   return L;
 }
 
-// Argument checks shared by the two decode entry points (no HIP call); on
+// Argument checks shared by the decode entry points (no kernel launch); on
 // success fills p (everything but the routing fields). B == 0 is accepted
-// before pointers are looked at.
+// before pointers are looked at. With own_scratch the partials go to the
+// library's static device scratch (set by the caller) instead of a workspace,
+// and the shape must fit it.
 gqa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* lens,
                           void* out, int B, int h, int g, int T_max, int d, gqa_dtype in_dtype,
                           gqa_dtype out_dtype, float scale, void* workspace, size_t workspace_bytes,
-                          gqa::DecodeParams& p) {
+                          gqa::DecodeParams& p, bool own_scratch = false) {
   if (B < 0 || T_max < 0) return fail(GQA_ERR_INVALID_ARG, "B=%d and T_max=%d must be >= 0", B, T_max);
   if (h < 1 || g < 1) return fail(GQA_ERR_INVALID_ARG, "h=%d and g=%d must be >= 1", h, g);
   if (h % g != 0) return fail(GQA_ERR_INVALID_ARG, "g=%d must divide h=%d", g, h);
@@ -116,10 +118,16 @@ gqa_status prepare_decode(const void* q, const void* k_cache, const void* v_cach
   if (!gqa::decode_supports(d)) return fail(GQA_ERR_UNSUPPORTED, "decode supports d in {64, 128}, got %d", d);
   if (h / g > 64) return fail(GQA_ERR_UNSUPPORTED, "decode supports h/g <= 64, got %d", h / g);
   const DecodeLayout L = decode_layout(h, g, d);
-  if (workspace_bytes < L.total)
-    return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, L.total);
-  if (!workspace || !aligned16(workspace))
-    return fail(GQA_ERR_INVALID_ARG, "workspace must be a 16-byte aligned device pointer");
+  if (own_scratch) {
+    if (L.total > gqa::kDecodeScratchBytes)
+      return fail(GQA_ERR_WORKSPACE, "this shape needs %zu bytes of split partials; the static scratch holds %zu",
+                  L.total, gqa::kDecodeScratchBytes);
+  } else {
+    if (workspace_bytes < L.total)
+      return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, L.total);
+    if (!workspace || !aligned16(workspace))
+      return fail(GQA_ERR_INVALID_ARG, "workspace must be a 16-byte aligned device pointer");
+  }
   p.q = q; p.k_cache = k_cache; p.v_cache = v_cache; p.lens = lens; p.out = out;
   p.B = B; p.h = h; p.g = g; p.T_max = T_max; p.d = d;
   p.n_units = L.n_units;
@@ -190,6 +198,23 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache, c
   if (s != GQA_OK || B == 0) return s;
   if ((s = check_device()) != GQA_OK) return s;
   return hip_status(gqa::launch_decode(p, static_cast<hipStream_t>(stream)), "gqa_decode launch");
+}
+
+gqa_status gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* lens,
+                              void* out, int B, int h, int g, int T_max, int d, gqa_dtype in_dtype,
+                              gqa_dtype out_dtype, float scale, void* stream) {
+  g_last_error[0] = '\0';
+  gqa::DecodeParams p{};
+  gqa_status s = prepare_decode(q, k_cache, v_cache, lens, out, B, h, g, T_max, d, in_dtype, out_dtype,
+                                scale, nullptr, 0, p, /*own_scratch=*/true);
+  if (s != GQA_OK || B == 0) return s;
+  if ((s = check_device()) != GQA_OK) return s;
+  void* scratch = nullptr;
+  if ((s = hip_status(gqa::decode_scratch(&scratch), "gqa_decode_noalloc scratch lookup")) != GQA_OK) return s;
+  const DecodeLayout L = decode_layout(h, g, d);
+  p.part_acc = static_cast<float*>(scratch);
+  p.part_ml = reinterpret_cast<float*>(static_cast<char*>(scratch) + L.acc_bytes);
+  return hip_status(gqa::launch_decode(p, static_cast<hipStream_t>(stream)), "gqa_decode_noalloc launch");
 }
 
 gqa_status gqe_routed_decode(const void* q, const void* k_cache, const void* v_cache,

@@ -40,6 +40,7 @@
 //    and are masked out of the softmax. Padding may hold anything, NaN
 //    included.
 #include <cstdlib>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -617,6 +618,38 @@ int decode_units(int h, int g, int d) {
   }
   (void)hipGetLastError();
   return n_cu * per_cu;
+}
+
+// Device scratch of the allocation-free decode entry point: the split
+// partials live in this array instead of a caller's workspace. Each device the
+// library runs on holds its own copy until the process ends. Host code must
+// never pass the array's name to a kernel or a copy (on the host it is only a
+// stand-in for the symbol): it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {

@@ -91,6 +91,11 @@ hipError_t launch_router(const RouterParams& p, hipStream_t stream);
 hipError_t launch_router_proj(const RouterProjParams& p, hipStream_t stream);
 hipError_t launch_wsum(const WsumParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+// Bytes of the static device scratch that the allocation-free decode uses for
+// its split partials, and its address on the current device (looked up with
+// hipGetSymbolAddress on the first call per device, then cached).
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+hipError_t decode_scratch(void** ptr);
 // Peak microbenchmarks: read `bytes` (a multiple of 16) of buf once and XOR
 // all 32-bit words into *x_out; run the MFMA-only loop, add the sum of its
 // accumulators to *sum_out and report the flops it performs.

@@ -134,6 +134,25 @@ gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gqa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and kernels as gqa_decode, with the split partials kept in
+ * a static device array of the library (16 MiB on every device the library
+ * runs on, held until the process ends) instead of a caller's workspace. The
+ * call itself allocates nothing. Arguments as for gqa_decode, without the
+ * workspace. All calls on one device share that array, so calls that overlap
+ * on one device race; consecutive calls on one stream are safe (every partial
+ * a call reads was written by that call, so the array needs no clearing).
+ * Returns GQA_ERR_WORKSPACE when the shape needs more partials than the array
+ * holds (gqa_decode_workspace_bytes(...) above 16 MiB), and GQA_ERR_HIP when
+ * the array's device address cannot be looked up.
+ */
+gqa_status gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* lens, void* out,
+                              int B, int h, int g, int T_max, int d,
+                              gqa_dtype in_dtype, gqa_dtype out_dtype, float scale, void* stream);
+
+/*
  * GQE layer output as the pages build it (gist.science explainer of "Grouped
  * Query Experts", section "Architecture et Routage", output construction):
  * the outputs of the k experts kept in every group, concatenated; a weighted

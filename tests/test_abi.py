@@ -300,3 +300,23 @@ def test_decode_empty_cache_accepts_its_workspace():
     assert st == NO_DEVICE, gq.last_error()
     st = lib.gqa_decode(P, None, None, P, P, 2, 8, 2, 0, 128, BF16, BF16, 0.1, P, ws - 1, None)
     assert st == WORKSPACE
+
+
+def _noalloc(B=4, h=32, g=8, T=8192, d=128, i=BF16):
+    return lib.gqa_decode_noalloc(P, P, P, P, P, B, h, g, T, d, i, BF16, 0.1, None)
+
+
+def test_decode_noalloc_checks(monkeypatch):
+    """The allocation-free decode takes gqa_decode's argument checks and
+    rejects, before any HIP call, shapes whose split partials exceed its
+    16 MiB static scratch."""
+    assert _noalloc(g=7) == INVALID
+    assert _noalloc(i=F32) == UNSUPPORTED
+    assert _noalloc(d=48) == UNSUPPORTED
+    assert _noalloc(B=0) == OK
+    monkeypatch.setenv("GQA_DECODE_UNITS", "100000")   # 100000 waves x 2 x 4 heads x 130 floats
+    assert _noalloc() == WORKSPACE
+    assert "16777216" in gq.last_error()
+    if not torch.cuda.is_available():
+        monkeypatch.setenv("GQA_DECODE_UNITS", "512")
+        assert _noalloc() == NO_DEVICE
