@@ -64,6 +64,7 @@ namespace {
 constexpr int kWavesLarge = 12, kBNLarge = 32, kOccLarge = 3;
 constexpr int kWavesSmall = 8, kBNSmall = 64, kOccSmall = 2;
 constexpr float kRescale = 8.0f;                      // lazy-rescale threshold, log2 units
+constexpr float kRescaleSum = 256.0f;                 // 2^kRescale: a lane's tile sum above it raises the reference
 
 template <int D, int W, int kBN>
 struct Tile {
@@ -260,7 +261,12 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   const uint16_t* vbase = a.v + b * a.kv_b + gam * a.kv_g;
   // Byte offsets (from the tile's first key row) that this lane loads for the
   // wave's DMA instructions j = wave + W*i: K granules first, then V.
-  uint32_t dma_off[L::kMine];
+  // The sequence's last key tile may be partial (T not a multiple of kBN):
+  // its rows past key T-1 load key T-1 instead (finite values that the mask
+  // discards), so nothing past the K/V tensors is read. Its offsets are
+  // formed once here; every tile then only selects between the two sets.
+  const int last_full = a.T - 1 - (div_up(a.T, kBN) - 1) * kBN;  // last valid row of the last tile
+  uint32_t dma_off[L::kMine], dma_off_last[L::kMine];
 #pragma unroll
   for (int i = 0; i < L::kMine; ++i) {
     const int j = wave_u + W * i;
@@ -271,9 +277,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
     if (row >= kBN) row = kBN - 1;  // rounding slack after the last row
     if (gr >= L::kCPR) gr = 0;      // pad granule
     dma_off[i] = (uint32_t)(row * D + gr * 8) * 2u;
+    dma_off_last[i] = (uint32_t)(min(row, last_full) * D + gr * 8) * 2u;
   }
-  // Start the DMA of key tile kt into buffer buf. Keys past T (last tile only)
-  // are clamped to key T-1: finite values that the mask discards.
+  // Start the DMA of key tile kt into buffer buf.
   auto issue_tile = [&](int kt, auto buf) {
     uint16_t* const Kb = buf.value ? K1 : K0;
     uint16_t* const Vb = buf.value ? V1 : V0;
@@ -284,11 +290,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
       const int j = wave_u + W * i;
       if (j >= L::kDma) break;
       const bool isk = j < L::kDmaK;
-      uint32_t off = dma_off[i];
-      if (!full) {
-        const int last = a.T - 1 - key0;  // >= 0: a tile is issued only if key0 < T
-        if ((int)(off / (2 * D)) > last) off = (uint32_t)last * (2 * D) + (off & (2 * D - 1));
-      }
+      const uint32_t off = full ? dma_off[i] : dma_off_last[i];
       const char* base = reinterpret_cast<const char*>((isk ? kbase : vbase) + (size_t)key0 * D);
       const uint16_t* src = reinterpret_cast<const uint16_t*>(base + off);
       uint16_t* dst = isk ? Kb + j * 512 : Vb + (j - L::kDmaK) * 512;
@@ -363,43 +365,57 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
       // Mask keys past the row's limit: (kb, i) holds key key0 + 32kb + 8(i/4) + 4hq + i%4.
       const bool need_mask = (a.causal && key0 + kBN - 1 > wt_lo) || (key0 + kBN > a.T);
       if (need_mask) {
-        const int lim = a.causal ? t_row : a.T - 1;
+        const int lim = (a.causal ? t_row : a.T - 1) - key0 - 4 * hq;
 #pragma unroll
         for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * hq + (i & 3);
-            if (key > lim) s[kb][i] = -INFINITY;
-          }
+          for (int i = 0; i < 16; ++i)
+            if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) s[kb][i] = -INFINITY;
       }
-      float mloc = -INFINITY;
+
+      // P^T as bf16 B operands: step u covers keys 16u .. 16u+15 of the tile.
+      // The probabilities are taken against the current reference max first;
+      // a score above it by more than kRescale (log2 units) shows as a
+      // probability above 2^kRescale, so as a partial row sum above it (a sum
+      // of probabilities each below 2^kRescale can exceed it too, which only
+      // costs an unneeded raise of the reference). Only then is the tile's max
+      // formed, the reference raised, the accumulators rescaled and the
+      // probabilities taken again. This keeps the max reduction off the path
+      // of every other tile. The row sum adds the rounded bf16 values, the
+      // ones the MFMA uses.
+      bf16x8 pf[kBN / 16];
+      float lt[2] = {0.0f, 0.0f};
+      auto probs = [&]() {
+        lt[0] = lt[1] = 0.0f;
 #pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
+        for (int u = 0; u < kBN / 16; ++u) {
+          float pv[8];
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) mloc = fmaxf(fmaxf(mloc, s[kb][i]), s[kb][i + 1]);
-      const float mloc_s = mloc * a.c;
-      if (__any(mloc_s > m_ref + kRescale)) {
+          for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + j], a.c, -m_ref));
+          pf[u] = pack_bf16x8(pv);
+          const bf16x2* pp = reinterpret_cast<const bf16x2*>(&pf[u]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) lt[u & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp[j], ones, lt[u & 1], false);
+        }
+      };
+      probs();
+      // NaN and infinity (the first tile, against m_ref = -inf) take the raise too.
+      if (__any(!(lt[0] + lt[1] <= kRescaleSum))) {
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) mloc = fmaxf(fmaxf(mloc, s[kb][i]), s[kb][i + 1]);
+        const float mloc_s = mloc * a.c;
         const float m_new = fmaxf(m_ref, fmaxf(mloc_s, __shfl_xor(mloc_s, 32)));
         const float alpha = fast_exp2(m_ref - m_new);
         m_ref = m_new;
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+        probs();
       }
-
-      // P^T as bf16 B operands: step u covers keys 16u .. 16u+15 of the tile.
-      // The row sum adds the rounded bf16 values, the ones the MFMA uses.
-      bf16x8 pf[kBN / 16];
-#pragma unroll
-      for (int u = 0; u < kBN / 16; ++u) {
-        float pv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(s[u >> 1][8 * (u & 1) + j], a.c, -m_ref));
-        pf[u] = pack_bf16x8(pv);
-        const bf16x2* pp = reinterpret_cast<const bf16x2*>(&pf[u]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[j], ones, l_run, false);
-      }
+      l_run += lt[0] + lt[1];
 
       // O^T += V^T P^T. Element j of step u is key 16u + 8(j/4) + 4hq + j%4,
       // which the two transposing reads fetch for d = 32db + l%32.
