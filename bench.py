@@ -417,6 +417,8 @@ def main():
         if peaks:
             line["roofline"]["measured_peak"] = peaks["mfma_bf16"]["TFLOPs"]
             line["roofline"]["frac_measured_peak"] = p["tflops"] / peaks["mfma_bf16"]["TFLOPs"]
+            line["roofline"]["attn_tile_loop_peak"] = peaks["attn_tile"]["TFLOPs"]
+            line["roofline"]["frac_attn_tile_loop_peak"] = p["tflops"] / peaks["attn_tile"]["TFLOPs"]
         line["prefill"] = {"mean_us": p["mean_ms"] * 1e3, "median_us": p["median_ms"] * 1e3,
                            "min_us": p["min_ms"] * 1e3, "flops_per_launch": p["flops_per_launch"]}
     if "decode" in res:
@@ -457,9 +459,10 @@ def main():
 def measured_peaks(torch, gq, dev):
     """The library's peak microbenchmarks, each timed as the median of 10
     launches with HIP events: an HBM read of a 4 GiB buffer (16 times the
-    Infinity Cache) and the MFMA-only loop, once as long as a prefill launch
-    and once long enough for the clock to settle under MFMA load. Also the
-    clocks and power cap rocm-smi reports."""
+    Infinity Cache), and the MFMA-only loop and the prefill's attention tile
+    loop (LDS fragment reads, MFMAs and softmax of one tile staged in LDS),
+    each once as long as a prefill launch and once long enough for the clock
+    to settle under MFMA load. Also the clocks and power cap rocm-smi reports."""
     out = {}
     buf = torch.randint(0, 256, (1 << 32,), dtype=torch.uint8, device=dev)
     xo = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -490,11 +493,30 @@ def measured_peaks(torch, gq, dev):
         ms = sorted(t.ms())
         out[key] = {"TFLOPs": flops / (ms[5] * 1e-3) / 1e12, "flops": flops, "iters": iters,
                     "median_us": ms[5] * 1e3, "min_us": ms[0] * 1e3}
+    # The prefill's attention tile loop with its operands staged in LDS once:
+    # the rate any kernel doing this per-tile work reaches on the chip, with
+    # no global memory traffic and no barrier.
+    g = torch.Generator(device=dev).manual_seed(12)
+    qkv = torch.randn(3, 32, 128, generator=g, device=dev).to(torch.bfloat16)
+    for key, iters in (("attn_tile", 300), ("attn_tile_sustained", 8000)):
+        for _ in range(3):
+            gq.peak_attn_tile(qkv, iters)
+        t = Timer(torch)
+        flops = 0.0
+        for _ in range(10):
+            gq.peak_hbm_read(buf[: 1 << 30], xo)
+            with t:
+                _, flops = gq.peak_attn_tile(qkv, iters)
+        torch.cuda.synchronize()
+        ms = sorted(t.ms())
+        out[key] = {"TFLOPs": flops / (ms[5] * 1e-3) / 1e12, "flops": flops, "iters": iters,
+                    "median_us": ms[5] * 1e3, "min_us": ms[0] * 1e3}
     del buf
     torch.cuda.empty_cache()
     log(f"measured peaks: HBM read {out['hbm_read']['GBps']:.0f} GB/s, "
         f"bf16 MFMA {out['mfma_bf16']['TFLOPs']:.0f} TFLOP/s "
-        f"({out['mfma_bf16_sustained']['TFLOPs']:.0f} sustained)")
+        f"({out['mfma_bf16_sustained']['TFLOPs']:.0f} sustained), attention tile loop "
+        f"{out['attn_tile']['TFLOPs']:.0f} TFLOP/s ({out['attn_tile_sustained']['TFLOPs']:.0f} sustained)")
     out["rocm_smi"] = rocm_smi_clocks()
     return out
 

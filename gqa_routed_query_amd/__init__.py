@@ -14,9 +14,10 @@ this package only marshals torch tensors into its entry points:
 * :func:`gqe_router` -- the router's projection x W_r^T fused with the top-k.
 * :func:`gqe_prefill_build` -- the GQE layer output: kept experts concatenated,
   their weighted-sum slot and the shared head.
-* :func:`peak_hbm_read`, :func:`peak_mfma_bf16` -- peak microbenchmarks (an
-  HBM read stream and an MFMA-only loop), the measured peaks the path's rates
-  are compared with.
+* :func:`peak_hbm_read`, :func:`peak_mfma_bf16`, :func:`peak_attn_tile` --
+  peak microbenchmarks (an HBM read stream, an MFMA-only loop, the prefill's
+  attention tile loop on register operands), the measured peaks the path's
+  rates are compared with.
 
 torch provides device memory and the stream; every step of the computation
 runs in the library's kernels. Importing the package fails loudly when the
@@ -39,6 +40,7 @@ from ._binding import (  # noqa: F401
     gqe_workspace_bytes,
     last_error,
     lib_path,
+    peak_attn_tile,
     peak_hbm_read,
     peak_mfma_bf16,
     status_string,

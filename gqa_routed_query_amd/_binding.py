@@ -61,6 +61,8 @@ def _load():
     lib.gqa_peak_hbm_read.argtypes = [vp, sz, vp, vp]
     lib.gqa_peak_mfma_bf16.restype = i32
     lib.gqa_peak_mfma_bf16.argtypes = [vp, i32, vp, ctypes.POINTER(ctypes.c_double), vp]
+    lib.gqa_peak_attn_tile.restype = i32
+    lib.gqa_peak_attn_tile.argtypes = [vp, i32, f32, vp, ctypes.POINTER(ctypes.c_double), vp]
     lib.gqe_prefill_build.restype = i32
     lib.gqe_prefill_build.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, i32, i32,
                                       i32, i32, i32, i32, i32, f32, i32, vp]
@@ -358,6 +360,25 @@ def peak_mfma_bf16(operands, iters: int, sum_out=None):
                                  _stream(dev))
     _check("gqa_peak_mfma_bf16", st)
     return sum_out, flops.value
+
+
+def peak_attn_tile(qkv, iters: int, scale: float | None = None, out=None):
+    """Peak microbenchmark: the prefill's attention tile loop on register
+    operands. qkv: bf16 device tensor [3, 32, 128] (q, k, v of one tile).
+    Returns (out, flops): out [32, 128] float32, the attention of the 32
+    queries over the 32 keys as one wave computed it; flops, the work of the
+    launch."""
+    dev = _dev(qkv)
+    if qkv.dtype != torch.bfloat16 or tuple(qkv.shape) != (3, 32, 128):
+        raise ValueError("qkv must be a contiguous bf16 tensor [3, 32, 128]")
+    if out is None:
+        out = torch.empty((32, 128), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(128) if scale is None else float(scale)
+    flops = ctypes.c_double(0.0)
+    st = _lib.gqa_peak_attn_tile(qkv.data_ptr(), int(iters), scale, out.data_ptr(), ctypes.byref(flops),
+                                 _stream(dev))
+    _check("gqa_peak_attn_tile", st)
+    return out, flops.value
 
 
 def gqe_prefill_build(q, q_shared, k, v, router_logits, top_k: int, shared_kv: int = 0,

@@ -383,4 +383,18 @@ gqa_status gqa_peak_mfma_bf16(const void* operands, int iters, float* sum_out, d
                     "gqa_peak_mfma_bf16 launch");
 }
 
+gqa_status gqa_peak_attn_tile(const void* qkv, int iters, float scale, float* out, double* flops, void* stream) {
+  g_last_error[0] = '\0';
+  if (iters < 1) return fail(GQA_ERR_INVALID_ARG, "iters=%d must be >= 1", iters);
+  if (!(std::isfinite(scale) && scale > 0.0f))
+    return fail(GQA_ERR_INVALID_ARG, "scale=%g must be finite and > 0", (double)scale);
+  if (!qkv || !out || !flops) return fail(GQA_ERR_INVALID_ARG, "null qkv, out or flops pointer");
+  if (!aligned16(qkv) || (reinterpret_cast<uintptr_t>(out) & 3u))
+    return fail(GQA_ERR_INVALID_ARG, "qkv must be 16-byte and out 4-byte aligned");
+  gqa_status s = check_device();
+  if (s != GQA_OK) return s;
+  return hip_status(gqa::launch_peak_attn_tile(qkv, iters, scale, out, flops, static_cast<hipStream_t>(stream)),
+                    "gqa_peak_attn_tile launch");
+}
+
 }  // extern "C"

@@ -101,6 +101,10 @@ hipError_t decode_scratch(void** ptr);
 // accumulators to *sum_out and report the flops it performs.
 hipError_t launch_peak_hbm_read(const void* buf, size_t bytes, unsigned* x_out, hipStream_t stream);
 hipError_t launch_peak_mfma_bf16(const void* operands, int iters, float* sum_out, double* flops, hipStream_t stream);
+// The attention tile loop on register operands (q, k, v of one 32x128 tile);
+// writes the normalised output of one wave and reports the flops.
+hipError_t launch_peak_attn_tile(const void* qkv, int iters, float scale, float* out, double* flops,
+                                 hipStream_t stream);
 
 // Head dims with a bf16 MFMA prefill kernel / an fp32-arithmetic kernel (fp32
 // inputs at every listed d, bf16 inputs at d 16 and 32) / a decode kernel.

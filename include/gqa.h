@@ -322,6 +322,27 @@ gqa_status gqa_peak_hbm_read(const void* buf, size_t bytes, uint32_t* xor_out, v
  */
 gqa_status gqa_peak_mfma_bf16(const void* operands, int iters, float* sum_out, double* flops, void* stream);
 
+/*
+ * gqa_peak_attn_tile: the attention tile loop of the bf16 prefill on one tile
+ * staged in LDS: per iteration, for one 32-key tile of 32 query rows (head dim
+ * 128), the K and V fragment reads from LDS, S^T = K Q^T (8
+ * v_mfma_f32_32x32x16_bf16), the online softmax with its bf16 rounding of P,
+ * and O^T += V^T P^T (8 more MFMAs), the same tile every iteration, twelve
+ * waves on every CU (three per SIMD), no global memory traffic and no barrier. The rate bounds any kernel that does this per-tile work on
+ * the device (IBM Think page, scaled dot-product attention; the ml-canon GQA
+ * function).
+ *   qkv   device memory, 16-byte aligned: q, k and v of one tile, each
+ *         [32][128] bf16 row-major.
+ *   scale the softmax scale (finite, > 0).
+ *   out   device [32][128] fp32, written: the normalised output of one wave,
+ *         i.e. softmax(scale q k^T) v over the 32 keys (the tile repeats).
+ *   flops host double, written: the flops the launch performs (counted as
+ *         16 MFMAs of 2*32*32*16 per wave and iteration).
+ * Errors: GQA_ERR_INVALID_ARG (iters < 1, bad scale, null or misaligned
+ * pointer), GQA_ERR_NO_DEVICE, GQA_ERR_HIP.
+ */
+gqa_status gqa_peak_attn_tile(const void* qkv, int iters, float scale, float* out, double* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -79,3 +79,27 @@ def test_peak_rates_are_plausible():
     say(f"peak rates: {gbps:.0f} GB/s, {tflops:.0f} TFLOP/s")
     assert 2000 < gbps < 8200
     assert 800 < tflops < 2600
+
+
+@pytest.mark.parametrize("iters", [1, 7, 300])
+def test_peak_attn_tile_computes_the_tile(iters):
+    """The attention tile loop repeats one 32-key tile, so its normalised
+    output is the attention of the 32 queries over the 32 keys: the oracle's
+    GQA prefill of one head without a mask, within the bf16 tolerance (P is
+    rounded to bf16). The flops are 16 MFMAs of 32x32x16 per wave (12 per CU)
+    and iteration."""
+    import gqa_routed_query_amd as gq
+    import oracle
+    from gpu_util import TOL_BF16, max_abs
+
+    d = dev()
+    g = torch.Generator().manual_seed(17 + iters)
+    qkv = torch.randn(3, 32, 128, generator=g).to(torch.bfloat16)
+    say(f"peak_attn_tile iters={iters}")
+    out, flops = gq.peak_attn_tile(qkv.to(d), iters)
+    torch.cuda.synchronize()
+    q, k, v = (qkv[i].view(1, 1, 32, 128) for i in range(3))
+    ref = oracle.gqa_ref(q, k, v, causal=False)[0, 0]
+    assert max_abs(out, ref) <= TOL_BF16
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert flops == n_cu * 12 * iters * 16 * (2 * 32 * 32 * 16)
