@@ -422,6 +422,203 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KArgs a) {
   }
 }
 
+// 17 to 32 query heads per KV group (MQA at h = 32): the shares, pieces and
+// staging of decode_kernel, with the group's heads as the 32 columns of
+// v_mfma_f32_32x32x16_bf16 -- the prefill kernel's layout: S^T of a 32-key
+// sub-block is one 32x32 accumulator, O^T four, and lane l holds head l % 32.
+// With the heads in 16-wide blocks a wave needs ~346 registers and spills, and
+// a CU holds one workgroup; in this form it stays within 256 (two workgroups
+// per CU) and does half the matrix work. Measured at 32 heads per group (B=32,
+// T=16384, 268 MB of cache) it streams at the same rate as one workgroup per
+// CU: the cache bytes already in flight were not what limited it there.
+template <int D, bool ROUTED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode32_kernel(KArgs a) {
+  using L = DTile<D>;
+  constexpr int kCP = D + 4;                     // combine row: D values, max, sum, 16-byte pitch
+  constexpr int kComb = kWaves * 32 * kCP;      // floats of the combine (32 heads per wave)
+  constexpr int kSmemBytes =
+      (kWaves * L::wElems * 2 > kComb * 4) ? kWaves * L::wElems * 2 : kComb * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int unit = blockIdx.x;
+  const long long total = total_keys(a, lane);
+  const long long share = share_of(total, a.n_units);
+  const long long start = (long long)unit * share;
+  if (start >= total) return;  // uniform over the block
+  const long long end = min(start + share, total);
+
+  const int l32 = lane & 31;
+  const int hq = lane >> 5;
+  const int grp = lane >> 4;
+  const int i16 = lane & 15;
+  uint16_t* Kw = reinterpret_cast<uint16_t*>(smem) + wave * L::wElems;
+  uint16_t* Vw = Kw + L::kElems;
+  // transposing V reads (A operand of O^T += V^T P^T), as in the prefill kernel
+  const int tr_row = 4 * hq + (i16 >> 2);
+  const int tr_col = 16 * (grp & 1) + 4 * (i16 & 3);
+
+  // cur: the piece being reduced (same on every wave). ld: the piece of the
+  // sub-block this wave has in flight (ld_pi its index, ld_sb its first key).
+  long long cur_pos = start;
+  Piece cur = locate(a, start, end - start, lane);
+  long long ld_pos = cur_pos;
+  Piece ld = cur;
+  int ld_pi = 0, ld_sb = cur.k0 + wave * kSub;
+  bool ld_ok = ld_sb < cur.k1 || next_sub(a, ld, ld_pos, end, ld_sb, ld_pi, wave);
+  if (ld_sb >= ld.k1) ld_ok = false;
+
+  u32x4 kr[L::kLoads], vr[L::kLoads];
+  if (ld_ok) load_sub<D>(a, ld, ld_sb, lane, kr, vr);
+  // Q^T (B operand of S^T = K Q^T): head l32, d = hq * D/2 + 8 st.
+  bf16x8 qf[D / 16];
+  float* comb = reinterpret_cast<float*>(smem);
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  for (int pi = 0;; ++pi) {
+    {
+      const int head = head_of<ROUTED>(a, cur.b, cur.gam, min(l32, a.R - 1));
+      const uint16_t* qrow = a.q + ((size_t)cur.b * a.h + head) * D + hq * (D / 2);
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 8 * st);
+        if (l32 >= a.R) x = bf16x8{};
+        qf[st] = x;
+      }
+    }
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.0f;
+    const int k1 = cur.k1;
+
+    // This wave's sub-blocks of the piece: keys k0 + 32*wave + 128*i.
+    while (ld_ok && ld_pi == pi) {
+#pragma unroll
+      for (int i = 0; i < L::kLoads; ++i) {
+        const int cidx = lane + 64 * i;
+        const int row = cidx / L::kCPR, col = (cidx % L::kCPR) * 8;
+        *reinterpret_cast<u32x4*>(Kw + row * L::kPitch + col) = kr[i];
+        *reinterpret_cast<u32x4*>(Vw + row * L::vPitch + col) = vr[i];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int cur_sb = ld_sb;
+      ld_ok = next_sub(a, ld, ld_pos, end, ld_sb, ld_pi, wave);
+      if (ld_ok) load_sub<D>(a, ld, ld_sb, lane, kr, vr);
+
+      // S^T[key][head]: lane holds keys cur_sb + 8(i/4) + 4hq + i%4 of head l32.
+      f32x16 s = f32x16{};
+      {
+        const uint16_t* krow = Kw + l32 * L::kPitch + hq * (D / 2);
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(krow + 8 * st), qf[st], s);
+      }
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (cur_sb + 8 * (i >> 2) + 4 * hq + (i & 3) >= k1) s[i] = -INFINITY;
+        mloc = fmaxf(mloc, s[i]);
+      }
+      const float m_cand = fmaxf(mloc, __shfl_xor(mloc, 32)) * a.c;
+      // Raise the reference max only when a score exceeds it by more than
+      // 2^kRescale; otherwise keep it (probabilities stay below 2^kRescale).
+      if (__any(m_cand > m_run + kRescale)) {
+        const float m_new = fmaxf(m_run, m_cand);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+      }
+      // P^T as bf16 B operands: element j of step u is key 16u + 8(j/4) + 4hq + j%4.
+      bf16x8 pf[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(fmaf(s[8 * u + j], a.c, -m_run));
+        pf[u] = pack_bf16x8(pv);
+        const bf16x2* pp = reinterpret_cast<const bf16x2*>(&pf[u]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) l_run = __builtin_amdgcn_fdot2_f32_bf16(pp[j], ones, l_run, false);
+      }
+      // O^T += V^T P^T, V^T by two transposing reads per step and 32-wide d block.
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint16_t* p0 = Vw + (16 * u + tr_row) * L::vPitch + tr_col;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          o[db] = mfma32x32x16(lds_read_tr_pair(p0 + 32 * db, p0 + 8 * L::vPitch + 32 * db), pf[u], o[db]);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+
+    // Combine the 4 waves through LDS, one head block at a time; write the
+    // output rows when the piece is the whole stream, else a partial in slot 0
+    // (the share's first piece) or 1 (its last).
+    const bool whole = cur.k0 == 0 && k1 == cur.len;
+    const int slot = pi == 0 ? 0 : 1;
+    {
+      const float lsum = l_run + __shfl_xor(l_run, 32);
+      __syncthreads();  // LDS is free: the staging buffers are consumed
+      float* w = comb + (wave * 32 + l32) * kCP;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          *reinterpret_cast<f32x4*>(w + 32 * db + 8 * i4 + 4 * hq) =
+              f32x4{o[db][4 * i4], o[db][4 * i4 + 1], o[db][4 * i4 + 2], o[db][4 * i4 + 3]};
+      if (hq == 0) {
+        w[D] = m_run;
+        w[D + 1] = lsum;
+      }
+      __syncthreads();
+      for (int x = tid; x < 32 * D; x += kThreads) {
+        const int e = x / D;
+        const int d = x - e * D;
+        if (e >= a.R) break;  // x only grows
+        float M = -INFINITY;
+#pragma unroll
+        for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, comb[(wv * 32 + e) * kCP + D]);
+        float acc = 0.0f, den = 0.0f;
+#pragma unroll
+        for (int wv = 0; wv < kWaves; ++wv) {
+          const float* src = comb + (wv * 32 + e) * kCP;
+          const float mw = src[D];
+          const float sc = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
+          acc += sc * src[d];
+          den += sc * src[D + 1];
+        }
+        if (whole) {
+          const int head = head_of<ROUTED>(a, cur.b, cur.gam, e);
+          const size_t off = ((size_t)cur.b * a.h + head) * D + d;
+          float y = acc / den;
+          if (ROUTED) y *= a.gate[((size_t)cur.b * a.g + cur.gam) * a.R + e];
+          if (a.out_bf16)
+            static_cast<uint16_t*>(a.out)[off] = static_cast<uint16_t>(pack_bf16x2(y, 0.0f) & 0xffffu);
+          else
+            static_cast<float*>(a.out)[off] = y;
+        } else {
+          const size_t prow = ((size_t)unit * 2 + slot) * a.R + e;
+          a.part_acc[prow * D + d] = acc;
+          if (d == 0) {
+            a.part_ml[prow * 2 + 0] = M;
+            a.part_ml[prow * 2 + 1] = den;
+          }
+        }
+      }
+    }
+    Piece n;
+    if (!next_piece(a, cur, cur_pos, end, n)) break;
+    cur = n;
+    __syncthreads();  // combine reads done before the staging buffers are rewritten
+  }
+}
+
 // One wave per (sequence, head): a stream cut over several shares has its
 // pieces merged by log-sum-exp; a sequence with no cached keys gets a zero
 // row, and so does (routed) a head the router did not keep. Streams that lie
@@ -454,7 +651,9 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
     }
   }
   // Global position of the stream, g * (keys of sequences before b) + gam *
-  // len, and the total, from one pass over lens.
+  // len, and the total, from one pass over lens (len is read first, so both
+  // loads share one memory latency).
+  const int len = seq_len(a, b);
   long long before = 0, total = 0;
   for (int bb = lane; bb < a.B; bb += 64) {
     const long long l = seq_len(a, bb);
@@ -466,7 +665,6 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
     before += __shfl_xor(before, o);
     total += __shfl_xor(total, o);
   }
-  const int len = seq_len(a, b);
   if (len == 0) {
 #pragma unroll
     for (int x = 0; x < EPL; ++x) {
@@ -491,20 +689,42 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
   auto prow_of = [&](int j) {
     return ((size_t)(u0 + j) * 2 + (j == 0 ? slot0 : 0)) * a.R + e;
   };
-  // Pieces in rounds of 64: lane j holds piece j's (max, sum); the
-  // accumulator loads do not depend on the max, so a round issues together.
+  // Pieces in rounds of 64: lane j holds piece j's (max, sum). The
+  // accumulator rows are read kBatch pieces at a time, every load of a batch
+  // issued before the first is used (a batch past the last piece re-reads the
+  // last one and weighs it 0), so a round costs a few memory latencies, not
+  // one per piece. The first batch is in flight while the max is reduced.
+  constexpr int kBatch = 16;
   float M = -INFINITY, den = 0.0f;
   float acc[EPL];
 #pragma unroll
   for (int x = 0; x < EPL; ++x) acc[x] = 0.0f;
   for (int j0 = 0; j0 < n; j0 += 64) {
     const int nj = min(64, n - j0);
-    float mj = -INFINITY, lj = 0.0f;
-    if (lane < nj) {
-      const size_t pr = prow_of(j0 + lane);
-      mj = a.part_ml[pr * 2];
-      lj = a.part_ml[pr * 2 + 1];
-    }
+    // Branch-free loads (lanes past the last piece re-read it), so the first
+    // batch issues in the same block as the (max, sum) loads.
+    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + prow_of(j0 + min(lane, nj - 1)) * 2);
+    float v[kBatch][EPL];
+    auto fetch = [&](int jb) {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const size_t pr = prow_of(j0 + min(jb + u, nj - 1));
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) v[u][x] = a.part_acc[pr * D + lane + 64 * x];
+      }
+    };
+    auto consume = [&](int jb, float scl) {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float sc = __shfl(scl, min(jb + u, 63));  // 0 past the last piece
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) acc[x] += sc * v[u][x];
+      }
+    };
+    fetch(0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of the reduction
+    const float mj = lane < nj ? ml.x : -INFINITY;
+    const float lj = lane < nj ? ml.y : 0.0f;
     float Mr = mj;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) Mr = fmaxf(Mr, __shfl_xor(Mr, o));
@@ -516,11 +736,11 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
     den = den * alpha + dj;
 #pragma unroll
     for (int x = 0; x < EPL; ++x) acc[x] *= alpha;
-    for (int j = 0; j < nj; ++j) {
-      const float sc = fast_exp2(__shfl(mj, j) - Mn);
-      const size_t pr = prow_of(j0 + j);
-#pragma unroll
-      for (int x = 0; x < EPL; ++x) acc[x] += sc * a.part_acc[pr * D + lane + 64 * x];
+    const float scl = lane < nj ? fast_exp2(mj - Mn) : 0.0f;  // lane j: piece j's weight
+    consume(0, scl);
+    for (int jb = kBatch; jb < nj; jb += kBatch) {
+      fetch(jb);
+      consume(jb, scl);
     }
     M = Mn;
   }
@@ -539,7 +759,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
 template <int D>
 const void* kernel_for_hb(int hb) {
   if (hb == 1) return reinterpret_cast<const void*>(&decode_kernel<D, 1, false>);
-  if (hb == 2) return reinterpret_cast<const void*>(&decode_kernel<D, 2, false>);
+  if (hb == 2) return reinterpret_cast<const void*>(&decode32_kernel<D, false>);
   if (hb <= 4) return reinterpret_cast<const void*>(&decode_kernel<D, 4, false>);
   return nullptr;
 }
@@ -557,7 +777,7 @@ hipError_t launch_dr(const KArgs& a, const dim3 grid, hipStream_t stream) {
   if (hb == 1)
     hipLaunchKernelGGL((decode_kernel<D, 1, ROUTED>), grid, block, 0, stream, a);
   else if (hb == 2)
-    hipLaunchKernelGGL((decode_kernel<D, 2, ROUTED>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode32_kernel<D, ROUTED>), grid, block, 0, stream, a);
   else if (hb <= 4)
     hipLaunchKernelGGL((decode_kernel<D, 4, ROUTED>), grid, block, 0, stream, a);
   else

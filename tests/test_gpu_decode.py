@@ -28,6 +28,8 @@ def _run(q, kc, vc, lens, out_dtype=torch.float32):
     (3, 16, 16, 300, 128, torch.float32),    # MHA
     (4, 16, 2, 400, 64, torch.float32),      # d = 64
     (2, 64, 1, 130, 128, torch.float32),     # 64 heads per group
+    (3, 24, 1, 500, 128, torch.float32),     # 17-32 heads per group: the 32-column kernel, 8 idle columns
+    (2, 32, 1, 400, 64, torch.bfloat16),     # 32 heads per group at d = 64
 ])
 def test_decode_shapes_poisoned_padding(B, h, g, T_max, d, out_dt):
     say(f"decode B={B} h={h} g={g} T_max={T_max} d={d} out={out_dt}")

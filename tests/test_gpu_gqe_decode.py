@@ -40,6 +40,7 @@ def _check(out, idx, gate, q, kc, vc, lens, lg, top_k):
     (4, 16, 2, 400, 64, 3, True, torch.float32),      # d = 64
     (2, 64, 1, 130, 128, 5, False, torch.float32),    # 64 heads per group
     (3, 8, 2, 500, 128, 4, False, torch.float32),     # every expert kept
+    (2, 32, 1, 300, 128, 20, True, torch.float32),    # 20 of 32 kept: the 32-column kernel
 ])
 def test_gqe_decode_shapes_poisoned_padding(B, h, g, T_max, d, top_k, ties, out_dt):
     say(f"gqe decode B={B} h={h} g={g} T_max={T_max} d={d} k={top_k} ties={ties} out={out_dt}")
