@@ -119,32 +119,47 @@ struct KArgs {
   uint8_t part[kMaxOrder];
   uint8_t sbi[kMaxOrder];
   uint16_t split[kMaxOrder];
+  uint16_t split_tile[kMaxOrder];  // row tile of split number i (read by the merge kernel)
   float* ws;
 };
 
-// Zero the output rows of heads the router did not keep, for the tokens whose
-// first row lies in this block's row range.
+// Zero rows of the heads the router did not keep, for the tokens whose first
+// row lies in this block's row range. Called once the block's attention and
+// output are done, with `kept` pointing to free LDS for one 64-bit mask per
+// token: the kept heads of every token are gathered first, all loads
+// independent, so the store loop that follows issues no loads. A workgroup
+// stores only some tens of GB/s, so these rows (3/4 of the output at r = 4,
+// k = 1) cost a few microseconds per block wherever they go; at the end they
+// delay neither the block's first tile nor, in the loop, its tile copies
+// (stores share the wait counter with the copies on this target).
 template <int D, int W>
-__device__ void zero_unselected_rows(const KArgs& a, int b, int gam, int row0, int n_rows) {
+__device__ void zero_unselected_rows(const KArgs& a, int b, int gam, int row0, int n_rows,
+                                     unsigned long long* kept) {
   constexpr int kThreads = W * 64, kRowsPerBlock = W * 32;
   const int R = a.R, r = a.r;
   const int t_lo = div_up(row0, R);
   const int t_hi = (min(row0 + kRowsPerBlock, n_rows) - 1) / R;
-  if (t_hi < t_lo) return;
+  if (t_hi < t_lo) return;  // uniform over the block
+  const int n_tok = t_hi - t_lo + 1;  // at most kRowsPerBlock
+  for (int i = threadIdx.x; i < n_tok; i += kThreads) {
+    const int32_t* sel = a.idx + ((size_t)(b * a.T + t_lo + i) * a.g + gam) * R;
+    unsigned long long m = 0;
+    for (int j = 0; j < R; ++j) {
+      const unsigned e = (unsigned)(sel[j] - gam * r);  // the kept head's place in its group
+      if (e < 64u) m |= 1ull << e;
+    }
+    kept[i] = m;
+  }
+  __syncthreads();
   constexpr int CPR = D / 8;
-  const int n_items = (t_hi - t_lo + 1) * r * CPR;
+  const int n_items = n_tok * r * CPR;
   for (int c = threadIdx.x; c < n_items; c += kThreads) {
     const int tt = c / (r * CPR);
     const int rem = c - tt * r * CPR;
     const int e = rem / CPR;
     const int ch = rem - e * CPR;
-    const int t = t_lo + tt;
-    const int head = gam * r + e;
-    const int32_t* sel = a.idx + ((size_t)(b * a.T + t) * a.g + gam) * R;
-    bool kept = false;
-    for (int j = 0; j < R; ++j) kept |= (sel[j] == head);
-    if (kept) continue;
-    const size_t off = b * a.o_b + head * a.o_h + t * a.o_t + ch * 8;
+    if ((kept[tt] >> e) & 1ull) continue;
+    const size_t off = b * a.o_b + (gam * r + e) * a.o_h + (t_lo + tt) * a.o_t + ch * 8;
     const u32x4 z = {0u, 0u, 0u, 0u};
     if (a.out_bf16) {
       __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + off));
@@ -192,8 +207,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   const int n_rows = a.T * R;
   const int row0 = tile * kRowsPerBlock;
   if (row0 >= n_rows) return;  // a shared-head problem has T rows, fewer than the routed ones when k > 1
-
-  if (ROUTED && a.zero_unselected && !shared && part <= 1) zero_unselected_rows<D, W>(a, b, gam, row0, n_rows);
 
   // Attention row rho (< n_rows): token, slot, head (a routed row's head is
   // the router's pick) and gate.
@@ -506,6 +519,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
     }
     if (pass + 1 < n_pass) __syncthreads();
   }
+  // The K/V buffers are free since the last tile's barrier.
+  static_assert(L::kElems * 2 >= kRowsPerBlock * 8, "the kept-head masks must fit in a K buffer");
+  if (ROUTED && a.zero_unselected && !shared && part <= 1)
+    zero_unselected_rows<D, W>(a, b, gam, row0, n_rows, reinterpret_cast<unsigned long long*>(K0));
 }
 
 // Merges the two parts of every key-split row tile. Per row the partial
@@ -520,9 +537,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(KArgs a) {
   static_assert(kRowsPerBlock % kRowsPerSub == 0, "merge sub-blocks must tile the row tile");
   const int sub = blockIdx.x % kSubs, sbg = blockIdx.x / kSubs;
   const int sb = sbg / a.BG, bg = sbg % a.BG;
-  int tile = 0;
-  for (int i = 0; i < a.n_order; ++i)
-    if (a.part[i] == 1 && a.sbi[i] == sb) tile = a.order[i];
+  const int tile = a.split_tile[sb];
   const int b = bg / a.g, gam = bg - b * a.g;  // split launches carry no shared head
   const int R = a.R, n_rows = a.T * R, row0 = tile * kRowsPerBlock;
   const float* const p1 = a.ws + (size_t)(sb * a.BG + bg) * 2 * ((size_t)kRowsPerBlock * (D + 2));
@@ -583,6 +598,7 @@ void set_order(KArgs& a, const OrderShape& s) {
     a.part[i] = v[i].part;
     a.sbi[i] = v[i].sbi;
     a.split[i] = v[i].split;
+    if (v[i].part == 1) a.split_tile[v[i].sbi] = v[i].tile;
   }
   a.n_order = (int)v.size();
 }
