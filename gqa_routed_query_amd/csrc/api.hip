@@ -342,12 +342,18 @@ gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v, const
   if (workspace && workspace_bytes < need)
     return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   auto st = static_cast<hipStream_t>(stream);
-  gqa::RouterParams rp{router_logits, topk_idx, topk_gate, B, T, h, g, top_k};
-  if ((s = hip_status(gqa::launch_router(rp, st), "gqe router launch")) != GQA_OK) return s;
+  // The bf16 attention kernel selects the kept heads itself (one launch less);
+  // the fp32-arithmetic kernel reads them from the router kernel.
+  const bool select_in_kernel = in_dtype == GQA_BF16 && gqa::attn_bf16_supports(d);
+  if (!select_in_kernel) {
+    gqa::RouterParams rp{router_logits, topk_idx, topk_gate, B, T, h, g, top_k};
+    if ((s = hip_status(gqa::launch_router(rp, st), "gqe router launch")) != GQA_OK) return s;
+  }
   gqa::AttnParams p{};
   p.q = q; p.k = k; p.v = v; p.out = out;
   p.idx = topk_idx;
   p.gate = topk_gate;
+  p.logits = select_in_kernel ? router_logits : nullptr;
   p.B = B; p.h = h; p.g = g; p.T = T; p.d = d;
   p.R = top_k;
   p.scale = scale;

@@ -53,6 +53,7 @@
 #include "common.h"
 #include "launch.h"
 #include "plan.h"
+#include "topk.h"
 
 namespace gqa {
 namespace {
@@ -90,8 +91,9 @@ struct KArgs {
   const uint16_t* k;
   const uint16_t* v;
   void* out;
-  const int32_t* idx;
-  const float* gate;
+  int32_t* idx;         // routed: kept heads (written here when logits is set)
+  float* gate;          // routed: their gates (likewise)
+  const float* logits;  // routed, selecting in the kernel: router logits [B, T, h]; else null
   int h, g, T, R, r;
   int n_row_tiles;
   int BG;
@@ -109,19 +111,38 @@ struct KArgs {
   void* out_sh;
   int sh_kv;
   // Causal grids: block band i (blocks i*BG .. i*BG + BG-1, one per problem)
-  // runs row tile order[i] when n_order > 0, else row tile n_row_tiles-1-i.
+  // runs slot i of the planned order when n_order > 0, else row tile
+  // n_row_tiles-1-i. A slot packs, in one 64-bit word read with one scalar
+  // load: its row tile (bits 0-15), key-split point (16-31), part (32-39) and
+  // split number sbi (40-47). Part 1 covers key tiles [0, split) of the row
+  // tile, part 2 [split, n_tiles), and each writes its partial result to
+  // workspace slot (sbi * BG + bg) * 2 + part - 1; part 0 covers them all.
   int n_order;
-  uint16_t order[kMaxOrder];
-  // Key-split slots (routed launches given a workspace): slot i covers key
-  // tiles [0, split[i]) of its row tile when part[i] == 1 and [split[i],
-  // n_tiles) when part[i] == 2, and writes its partial result to workspace
-  // slot (sbi[i] * BG + bg) * 2 + part[i] - 1; part[i] == 0 covers them all.
-  uint8_t part[kMaxOrder];
-  uint8_t sbi[kMaxOrder];
-  uint16_t split[kMaxOrder];
-  uint16_t split_tile[kMaxOrder];  // row tile of split number i (read by the merge kernel)
+  uint64_t slot[kMaxOrder];
+  uint32_t split_tile[kMaxOrder];  // row tile of split number i (read by the merge kernel)
   float* ws;
 };
+
+__host__ __device__ inline int slot_tile(uint64_t s) { return (int)(s & 0xffffu); }
+__host__ __device__ inline int slot_split(uint64_t s) { return (int)((s >> 16) & 0xffffu); }
+__host__ __device__ inline int slot_part(uint64_t s) { return (int)((s >> 32) & 0xffu); }
+__host__ __device__ inline int slot_sbi(uint64_t s) { return (int)((s >> 40) & 0xffu); }
+
+// The router's selection for token t of (b, gam), made in the kernel from the
+// logits: returns the kept-head mask and sets the slot-th kept head's group
+// position and gate. Groups of up to 8 heads load their logits together into
+// registers; larger ones read them from memory as the selection goes.
+__device__ inline unsigned long long route_token(const KArgs& a, int b, int t, int gam, int slot, int* e,
+                                                 float* gate) {
+  const float* lg = a.logits + ((size_t)b * a.T + t) * a.h + gam * a.r;
+  if (a.r <= 8) {
+    float v[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) v[x] = x < a.r ? lg[x] : 0.0f;
+    return topk_rank_reg(v, a.r, a.R, slot, e, gate);
+  }
+  return topk_rank([&](int x) { return lg[x]; }, a.r, a.R, slot, e, gate);
+}
 
 // Zero rows of the heads the router did not keep, for the tokens whose first
 // row lies in this block's row range. Called once the block's attention and
@@ -142,11 +163,17 @@ __device__ void zero_unselected_rows(const KArgs& a, int b, int gam, int row0, i
   if (t_hi < t_lo) return;  // uniform over the block
   const int n_tok = t_hi - t_lo + 1;  // at most kRowsPerBlock
   for (int i = threadIdx.x; i < n_tok; i += kThreads) {
-    const int32_t* sel = a.idx + ((size_t)(b * a.T + t_lo + i) * a.g + gam) * R;
     unsigned long long m = 0;
-    for (int j = 0; j < R; ++j) {
-      const unsigned e = (unsigned)(sel[j] - gam * r);  // the kept head's place in its group
-      if (e < 64u) m |= 1ull << e;
+    if (a.logits) {
+      int e_unused;
+      float g_unused;
+      m = route_token(a, b, t_lo + i, gam, 0, &e_unused, &g_unused);
+    } else {
+      const int32_t* sel = a.idx + ((size_t)(b * a.T + t_lo + i) * a.g + gam) * R;
+      for (int j = 0; j < R; ++j) {
+        const unsigned e = (unsigned)(sel[j] - gam * r);  // the kept head's place in its group
+        if (e < 64u) m |= 1ull << e;
+      }
     }
     kept[i] = m;
   }
@@ -192,8 +219,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   const int bid = blockIdx.x;
   const int bg = bid % a.BG;
   const int band = bid / a.BG;
-  const int tile = !a.causal ? band : a.n_order ? (int)a.order[band] : a.n_row_tiles - 1 - band;
-  const int part = a.n_order ? (int)a.part[band] : 0;
+  const uint64_t sl = a.n_order ? a.slot[__builtin_amdgcn_readfirstlane(band)] : 0;
+  const int tile = !a.causal ? band : a.n_order ? slot_tile(sl) : a.n_row_tiles - 1 - band;
+  const int part = slot_part(sl);
   // The shared head's problem (uniform per block; only routed launches carry one).
   const bool shared = ROUTED && bg >= a.BG_main;
   const int b = shared ? bg - a.BG_main : bg / a.g;
@@ -222,9 +250,15 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
     if (shared) {
       ri.head = 0;
     } else if (ROUTED) {
-      const size_t o = ((size_t)(b * a.T + ri.t) * a.g + gam) * a.R + ri.slot;
-      ri.head = a.idx[o];
-      ri.gate = a.out_slots ? 1.0f : a.gate[o];
+      if (a.logits) {
+        int e;
+        route_token(a, b, ri.t, gam, ri.slot, &e, &ri.gate);
+        ri.head = gam * a.r + e;
+      } else {
+        const size_t o = ((size_t)(b * a.T + ri.t) * a.g + gam) * a.R + ri.slot;
+        ri.head = a.idx[o];
+        ri.gate = a.out_slots ? 1.0f : a.gate[o];
+      }
     } else {
       ri.head = gam * a.r + ri.slot;
     }
@@ -243,8 +277,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   const int t_last = (min(row0 + kRowsPerBlock, n_rows) - 1) / R;
   const int n_keys = a.causal ? t_last + 1 : a.T;
   const int n_tiles = div_up(n_keys, kBN);
-  const int kt_lo = part == 2 ? (int)a.split[band] : 0;
-  const int kt_hi = part == 1 ? (int)a.split[band] : n_tiles;
+  const int kt_lo = part == 2 ? slot_split(sl) : 0;
+  const int kt_hi = part == 1 ? slot_split(sl) : n_tiles;
 
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   uint16_t* const QOw = QO + wave_u * kQElems;
@@ -254,6 +288,14 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   if (hq == 0) {
     const RowInfo ri = row_info(min(rho, n_rows - 1));
     tab[l32] = make_int4(ri.t, ri.head, ri.slot, __float_as_int(ri.gate));
+    // Selecting in the kernel: each (token, slot) entry of idx and gate is
+    // written once, by the lane of its row in the block that owns the row's
+    // output (the first part of a key-split row tile).
+    if (ROUTED && a.logits && !shared && part <= 1 && rho < n_rows) {
+      const size_t o = ((size_t)(b * a.T + ri.t) * a.g + gam) * a.R + ri.slot;
+      a.idx[o] = ri.head;
+      a.gate[o] = ri.gate;
+    }
   }
   __syncthreads();
   // The wave's 32 Q rows into QOw by DMA, granule by granule as for K (pad
@@ -459,7 +501,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const bool partial = part != 0;
   float* const pws =
-      partial ? a.ws + ((size_t)(a.sbi[band] * a.BG + bg) * 2 + part - 1) * ((size_t)kRowsPerBlock * (D + 2))
+      partial ? a.ws + ((size_t)(slot_sbi(sl) * a.BG + bg) * 2 + part - 1) * ((size_t)kRowsPerBlock * (D + 2))
               : nullptr;
   if (partial && hq == 0) {
     pws[kRowsPerBlock * D + wave * 32 + l32] = m_ref;
@@ -594,10 +636,8 @@ void set_order(KArgs& a, const OrderShape& s) {
   if (it == cache.end()) it = cache.emplace(s, plan_order(s)).first;
   const std::vector<Slot>& v = it->second;
   for (size_t i = 0; i < v.size(); ++i) {
-    a.order[i] = v[i].tile;
-    a.part[i] = v[i].part;
-    a.sbi[i] = v[i].sbi;
-    a.split[i] = v[i].split;
+    a.slot[i] = (uint64_t)v[i].tile | ((uint64_t)v[i].split << 16) | ((uint64_t)v[i].part << 32) |
+                ((uint64_t)v[i].sbi << 40);
     if (v[i].part == 1) a.split_tile[v[i].sbi] = v[i].tile;
   }
   a.n_order = (int)v.size();
@@ -612,7 +652,7 @@ hipError_t launch_dw(KArgs a, const AttnParams& p, hipStream_t stream, int n_cu)
                           a.BG == a.BG_main ? max_split : 0});
   a.ws = static_cast<float*>(p.split_ws);
   int n_split = 0;
-  for (int i = 0; i < a.n_order; ++i) n_split += a.part[i] == 1;
+  for (int i = 0; i < a.n_order; ++i) n_split += slot_part(a.slot[i]) == 1;
   const dim3 grid((a.n_order ? a.n_order : a.n_row_tiles) * a.BG), block(W * 64);
   if (p.idx)
     hipLaunchKernelGGL((attn_bf16_kernel<D, W, BN, OCC, true>), grid, block, 0, stream, a);
@@ -658,8 +698,9 @@ hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
   a.k = static_cast<const uint16_t*>(p.k);
   a.v = static_cast<const uint16_t*>(p.v);
   a.out = p.out;
-  a.idx = p.idx;
-  a.gate = p.gate;
+  a.idx = const_cast<int32_t*>(p.idx);
+  a.gate = const_cast<float*>(p.gate);
+  a.logits = p.logits;
   a.h = p.h;
   a.g = p.g;
   a.T = p.T;

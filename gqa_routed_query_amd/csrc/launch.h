@@ -21,6 +21,9 @@ struct AttnParams {
   void* out;            // [B, h, T, d]
   const int32_t* idx;   // routed only: [B, T, g, R] global head ids, else null
   const float* gate;    // routed only: [B, T, g, R], else null
+  // Routed bf16 launches only (null: idx and gate are inputs): router logits
+  // [B, T, h]; the kernel selects the kept heads itself and writes idx and gate.
+  const float* logits;
   int B, h, g, T, d;
   int R;                // rows per token
   float scale;          // > 0
