@@ -283,35 +283,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   uint16_t* const QOw = QO + wave_u * kQElems;
   int4* const tab = rowtab + wave_u * 32;
-  // Each lane resolves its own row once (rows past the end stand in as the
-  // last row); lanes that move other rows read them from the table.
-  if (hq == 0) {
-    const RowInfo ri = row_info(min(rho, n_rows - 1));
-    tab[l32] = make_int4(ri.t, ri.head, ri.slot, __float_as_int(ri.gate));
-    // Selecting in the kernel: each (token, slot) entry of idx and gate is
-    // written once, by the lane of its row in the block that owns the row's
-    // output (the first part of a key-split row tile).
-    if (ROUTED && a.logits && !shared && part <= 1 && rho < n_rows) {
-      const size_t o = ((size_t)(b * a.T + ri.t) * a.g + gam) * a.R + ri.slot;
-      a.idx[o] = ri.head;
-      a.gate[o] = ri.gate;
-    }
-  }
-  __syncthreads();
-  // The wave's 32 Q rows into QOw by DMA, granule by granule as for K (pad
-  // granules receive a copy of granule 0).
-#pragma unroll
-  for (int j = 0; j < kQDma; ++j) {
-    const int p = j * 64 + lane;
-    int row = p / L::kGPR, gr = p - row * L::kGPR;
-    if (row > 31) row = 31;
-    if (gr >= L::kCPR) gr = 0;
-    const int4 ri = tab[row];
-    const uint16_t* src = (shared ? a.q_sh + (size_t)b * a.T * D : a.q + b * a.q_b + (size_t)ri.y * a.q_h) +
-                          (size_t)ri.x * D + gr * 8;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(QOw + j * 512), 16, 0, 0);
-  }
-
   const uint16_t* kbase = a.k + b * a.kv_b + gam * a.kv_g;
   const uint16_t* vbase = a.v + b * a.kv_b + gam * a.kv_g;
   // Byte offsets (from the tile's first key row) that this lane loads for the
@@ -353,6 +324,41 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
     }
   };
 
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  // The first key tile does not depend on the row table: its copy is in
+  // flight while the rows are resolved and Q is requested.
+  issue_tile(kt_lo, B0{});
+
+  // Each lane resolves its own row once (rows past the end stand in as the
+  // last row); lanes that move other rows read them from the table.
+  if (hq == 0) {
+    const RowInfo ri = row_info(min(rho, n_rows - 1));
+    tab[l32] = make_int4(ri.t, ri.head, ri.slot, __float_as_int(ri.gate));
+    // Selecting in the kernel: each (token, slot) entry of idx and gate is
+    // written once, by the lane of its row in the block that owns the row's
+    // output (the first part of a key-split row tile).
+    if (ROUTED && a.logits && !shared && part <= 1 && rho < n_rows) {
+      const size_t o = ((size_t)(b * a.T + ri.t) * a.g + gam) * a.R + ri.slot;
+      a.idx[o] = ri.head;
+      a.gate[o] = ri.gate;
+    }
+  }
+  __syncthreads();
+  // The wave's 32 Q rows into QOw by DMA, granule by granule as for K (pad
+  // granules receive a copy of granule 0).
+#pragma unroll
+  for (int j = 0; j < kQDma; ++j) {
+    const int p = j * 64 + lane;
+    int row = p / L::kGPR, gr = p - row * L::kGPR;
+    if (row > 31) row = 31;
+    if (gr >= L::kCPR) gr = 0;
+    const int4 ri = tab[row];
+    const uint16_t* src = (shared ? a.q_sh + (size_t)b * a.T * D : a.q + b * a.q_b + (size_t)ri.y * a.q_h) +
+                          (size_t)ri.x * D + gr * 8;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(QOw + j * 512), 16, 0, 0);
+  }
+
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
@@ -371,9 +377,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   const int tr_col = 16 * (grp & 1) + 4 * (i16 & 3);
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  issue_tile(kt_lo, B0{});
   __syncthreads();
 
   // Q^T fragments: B operand of S^T = K Q^T. Lane half hq holds d in
