@@ -19,7 +19,9 @@ lens[b] (plus q and out).
 
 After the timed steps, the KV-group sweep (decode, B=32, T=16384, g in
 {1, 4, 8, 32}) is timed the same way, with the HBM bytes the counters measured
-per g (profiles/traffic_counters.json) beside the cache-size law, and the
+per g (profiles/traffic_counters.json) beside the cache-size law and, as the
+size-matched ceiling, the HBM read microbenchmark streaming the same cache
+bytes (one launch, flushed, same events), and the
 float64 CPU oracle is timed on the whole prefill workload (cpu_baseline); its
 output is compared with the GPU's, element by element.
 
@@ -269,8 +271,15 @@ def main():
         n_warm, n_time = (1, 1) if args.only == "sweep" else (3, 10)
         kv_mha = gq.gqa_kv_cache_bytes(ws.B, ws.h, ws.T, ws.d)
         for g in ws.g_sweep:
-            q, kc, vc, lens = decode_inputs(ws.B, ws.h, g, ws.T, ws.d, ws.lens, seed=ws.seed + g,
-                                            device=dev)
+            q, kc0, vc0, lens = decode_inputs(ws.B, ws.h, g, ws.T, ws.d, ws.lens, seed=ws.seed + g,
+                                              device=dev)
+            # K and V as two halves of one buffer, so that the HBM read
+            # microbenchmark can stream exactly the cache bytes in one launch
+            kv_buf = torch.empty((2,) + tuple(kc0.shape), dtype=kc0.dtype, device=dev)
+            kv_buf[0].copy_(kc0)
+            kv_buf[1].copy_(vc0)
+            del kc0, vc0
+            kc, vc = kv_buf[0], kv_buf[1]
             out = torch.empty_like(q)
             wsb = torch.empty(max(gq.gqa_decode_workspace_bytes(ws.B, ws.h, g, ws.T, ws.d), 1),
                               dtype=torch.uint8, device=dev)
@@ -284,6 +293,19 @@ def main():
                     gq.gqa_decode(q, kc, vc, lens, out=out, workspace=wsb)
             torch.cuda.synchronize()
             st = stats(tm.ms())
+            # the same cache bytes as one plain sequential read (flushed, same
+            # timing): what any kernel that must read them can reach at this size
+            tr = Timer(torch)
+            xr = torch.zeros(1, dtype=torch.int32, device=dev)
+            for it in range(n_warm + n_time):
+                flush.sum()
+                if it < n_warm:
+                    gq.peak_hbm_read(kv_buf, xr)
+                    continue
+                with tr:
+                    gq.peak_hbm_read(kv_buf, xr)
+            torch.cuda.synchronize()
+            rd = stats(tr.ms())
             # the cache-size law 2 * n_kv * d * T * sizeof(bf16) * B, and the HBM
             # bytes the counters measured for one call (null when they were
             # taken on another kernel source)
@@ -295,9 +317,13 @@ def main():
                               measured_read_bytes=measured,
                               measured_read_over_law=(measured / kv) if measured else None,
                               mean_ms=st["mean_ms"], GBps=nbytes / (st["mean_ms"] * 1e-3) / 1e9,
-                              frac_peak=nbytes / (st["mean_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS))
-            log(f"sweep g={g}: {st['mean_ms']*1e3:.1f} us, {sweep[-1]['GBps']:.0f} GB/s")
-            del q, kc, vc, out, wsb
+                              frac_peak=nbytes / (st["mean_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                              read_same_bytes_us=rd["mean_ms"] * 1e3,
+                              read_same_bytes_GBps=kv / (rd["mean_ms"] * 1e-3) / 1e9,
+                              frac_of_read_same_bytes=rd["mean_ms"] / st["mean_ms"]))
+            log(f"sweep g={g}: {st['mean_ms']*1e3:.1f} us, {sweep[-1]['GBps']:.0f} GB/s; plain read of the "
+                f"same {kv/1e6:.0f} MB {rd['mean_ms']*1e3:.1f} us ({sweep[-1]['read_same_bytes_GBps']:.0f} GB/s)")
+            del q, kc, vc, kv_buf, out, wsb
             torch.cuda.empty_cache()
 
     # ---- GQE router with its projection (x W_r^T + top-k), outside the step ----
