@@ -632,7 +632,11 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
   const int head = row - b * a.h;
   const int gam = head / a.r;
   int e = head - gam * a.r;  // the head's row in its group
-  constexpr int EPL = D / 64;
+  // Columns per lane: D/64, or one for D = 32, where lanes 32-63 read column
+  // D-1 (in bounds) and write nothing.
+  constexpr int EPL = D >= 64 ? D / 64 : 1;
+  const bool col_ok = D >= 64 || lane < D;
+  const int col = D >= 64 ? lane : min(lane, D - 1);
   if (ROUTED) {
     const int32_t* sel = a.idx + ((size_t)b * a.g + gam) * a.R;
     e = -1;
@@ -641,7 +645,8 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
     if (e < 0) {
 #pragma unroll
       for (int x = 0; x < EPL; ++x) {
-        const size_t off = (size_t)row * D + lane + 64 * x;
+        const size_t off = (size_t)row * D + col + 64 * x;
+        if (!col_ok) break;
         if (a.out_bf16)
           static_cast<uint16_t*>(a.out)[off] = 0;
         else
@@ -668,7 +673,8 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
   if (len == 0) {
 #pragma unroll
     for (int x = 0; x < EPL; ++x) {
-      const size_t off = (size_t)row * D + lane + 64 * x;
+      const size_t off = (size_t)row * D + col + 64 * x;
+      if (!col_ok) break;
       if (a.out_bf16)
         static_cast<uint16_t*>(a.out)[off] = 0;
       else
@@ -710,7 +716,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
       for (int u = 0; u < kBatch; ++u) {
         const size_t pr = prow_of(j0 + min(jb + u, nj - 1));
 #pragma unroll
-        for (int x = 0; x < EPL; ++x) v[u][x] = a.part_acc[pr * D + lane + 64 * x];
+        for (int x = 0; x < EPL; ++x) v[u][x] = a.part_acc[pr * D + col + 64 * x];
       }
     };
     auto consume = [&](int jb, float scl) {
@@ -747,8 +753,9 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
   const float inv = (ROUTED ? a.gate[((size_t)b * a.g + gam) * a.R + e] : 1.0f) / den;
 #pragma unroll
   for (int x = 0; x < EPL; ++x) {
+    if (!col_ok) break;
     const float y = acc[x] * inv;
-    const size_t off = (size_t)row * D + lane + 64 * x;
+    const size_t off = (size_t)row * D + col + 64 * x;
     if (a.out_bf16)
       static_cast<uint16_t*>(a.out)[off] = static_cast<uint16_t>(pack_bf16x2(y, 0.0f) & 0xffffu);
     else
@@ -765,6 +772,7 @@ const void* kernel_for_hb(int hb) {
 }
 
 const void* decode_kernel_for(int d, int hb) {
+  if (d == 32) return kernel_for_hb<32>(hb);
   if (d == 64) return kernel_for_hb<64>(hb);
   if (d == 128) return kernel_for_hb<128>(hb);
   return nullptr;
@@ -816,7 +824,7 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
 
 }  // namespace
 
-bool decode_supports(int d) { return d == 64 || d == 128; }
+bool decode_supports(int d) { return d == 32 || d == 64 || d == 128; }
 
 int decode_units(int h, int g, int d) {
   if (const char* env = std::getenv("GQA_DECODE_UNITS")) {
@@ -874,6 +882,7 @@ hipError_t decode_scratch(void** ptr) {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   switch (p.d) {
+    case 32: return launch_d<32>(p, stream);
     case 64: return launch_d<64>(p, stream);
     case 128: return launch_d<128>(p, stream);
     default: return hipErrorInvalidValue;

@@ -30,6 +30,9 @@ def _run(q, kc, vc, lens, out_dtype=torch.float32):
     (2, 64, 1, 130, 128, torch.float32),     # 64 heads per group
     (3, 24, 1, 500, 128, torch.float32),     # 17-32 heads per group: the 32-column kernel, 8 idle columns
     (2, 32, 1, 400, 64, torch.bfloat16),     # 32 heads per group at d = 64
+    (4, 16, 4, 600, 32, torch.float32),      # d = 32, 4 heads per group
+    (3, 32, 1, 500, 32, torch.bfloat16),     # d = 32, 32 heads per group (the 32-column kernel)
+    (2, 48, 1, 300, 32, torch.float32),      # d = 32, 48 heads per group
 ])
 def test_decode_shapes_poisoned_padding(B, h, g, T_max, d, out_dt):
     say(f"decode B={B} h={h} g={g} T_max={T_max} d={d} out={out_dt}")
