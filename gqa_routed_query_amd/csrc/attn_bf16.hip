@@ -64,6 +64,8 @@ namespace {
 // two workgroups' worth of work (short routed problems).
 constexpr int kWavesLarge = 12, kBNLarge = 32, kOccLarge = 3;
 constexpr int kWavesSmall = 8, kBNSmall = 64, kOccSmall = 2;
+// 16 raw bytes at an address that is only 8-byte aligned (staged bf16 output rows).
+typedef unsigned u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));
 constexpr float kRescale = 8.0f;                      // lazy-rescale threshold, log2 units
 constexpr float kRescaleSum = 256.0f;                 // 2^kRescale: a lane's tile sum above it raises the reference
 
@@ -344,7 +346,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
       a.gate[o] = ri.gate;
     }
   }
-  __syncthreads();
+  // The table is the wave's own and one wave's LDS accesses take effect in
+  // order, so its rows are read back below without a barrier. (A block
+  // barrier here would first wait for the copy of the first K/V tile, and
+  // only then let the Q copy start.)
   // The wave's 32 Q rows into QOw by DMA, granule by granule as for K (pad
   // granules receive a copy of granule 0).
 #pragma unroll
@@ -511,12 +516,17 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
     pws[kRowsPerBlock * (D + 1) + wave * 32 + l32] = l_tot;
   }
   const float inv = partial ? 1.0f : __int_as_float(tab[l32].w) / l_tot;
-  constexpr int kRowB = L::kPitch * 2;      // staged row pitch, bytes
   constexpr int kG = D * 2 / 16;            // 16-byte granules per staged row
   constexpr int kRowsPer = 64 / kG;         // rows per store instruction
   char* const stage = reinterpret_cast<char*>(QOw);
   const bool bf16_out = a.out_bf16 && !partial;
   const int n_pass = bf16_out ? 1 : 2;
+  // Staged row pitch in bytes. A bf16 row is staged by 8-byte writes, one
+  // per lane and row; at an odd multiple of 8 bytes the 32 rows of a write
+  // fall in distinct banks (at the Q pitch, rows 16 apart share them). Its
+  // 16-byte reads are then only 8-byte aligned. fp32 rows are staged by
+  // 16-byte writes at the Q pitch.
+  const int kRowB = bf16_out ? L::kPitch * 2 - 8 : L::kPitch * 2;
   for (int pass = 0; pass < n_pass; ++pass) {
     // o[db][4*i4 + j] holds d = 32db + 8i4 + 4hq + j of this lane's row.
     if (bf16_out) {
@@ -542,17 +552,29 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
         }
       }
     }
-    __syncthreads();
+    // Each wave reads back only the rows it staged; one wave's LDS accesses
+    // take effect in order, so no barrier is needed here.
+    // All of the wave's staged rows (and their table entries) are read before
+    // the first store, so the reads wait for LDS once rather than per store.
+    constexpr int kIt = 32 / kRowsPer;
+    u32x4 vs[kIt];
+    int4 rs[kIt];
 #pragma unroll
-    for (int i = 0; i < 32 / kRowsPer; ++i) {
+    for (int i = 0; i < kIt; ++i) {
+      const int row = i * kRowsPer + lane / kG;
+      vs[i] = *reinterpret_cast<const u32x4_a8*>(stage + row * kRowB + (lane % kG) * 16);
+      rs[i] = tab[row];
+    }
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
       const int row = i * kRowsPer + lane / kG;
       const int gran = lane % kG;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * kRowB + gran * 16);
+      const u32x4 v = vs[i];
       const int rr = wrow0 + row;
       if (partial) {
         *reinterpret_cast<u32x4*>(pws + (size_t)(wave * 32 + row) * D + pass * (D / 2) + gran * 4) = v;
       } else if (rr < n_rows) {
-        const int4 ri = tab[row];
+        const int4 ri = rs[i];
         const int oslot = a.out_slots ? gam * a.R + ri.z : ri.y;
         const size_t orow = shared ? ((size_t)b * a.T + ri.x) * D : b * a.o_b + oslot * a.o_h + ri.x * a.o_t;
         char* const outp = static_cast<char*>(shared ? a.out_sh : a.out);
@@ -562,7 +584,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(outp + ob));
       }
     }
-    if (pass + 1 < n_pass) __syncthreads();
   }
   // The K/V buffers are free since the last tile's barrier.
   static_assert(L::kElems * 2 >= kRowsPerBlock * 8, "the kept-head masks must fit in a K buffer");
