@@ -150,11 +150,11 @@ __device__ inline unsigned long long route_token(const KArgs& a, int b, int t, i
 // row lies in this block's row range. Called once the block's attention and
 // output are done, with `kept` pointing to free LDS for one 64-bit mask per
 // token: the kept heads of every token are gathered first, all loads
-// independent, so the store loop that follows issues no loads. A workgroup
-// stores only some tens of GB/s, so these rows (3/4 of the output at r = 4,
-// k = 1) cost a few microseconds per block wherever they go; at the end they
-// delay neither the block's first tile nor, in the loop, its tile copies
-// (stores share the wait counter with the copies on this target).
+// independent, so the store loop that follows issues no loads. These rows
+// (3/4 of the output at r = 4, k = 1) cost a few microseconds per block
+// wherever they go; at the end they delay neither the block's first tile nor,
+// in the loop, its tile copies (stores share the wait counter with the copies
+// on this target).
 template <int D, int W>
 __device__ void zero_unselected_rows(const KArgs& a, int b, int gam, int row0, int n_rows,
                                      unsigned long long* kept) {
@@ -180,22 +180,33 @@ __device__ void zero_unselected_rows(const KArgs& a, int b, int gam, int row0, i
     kept[i] = m;
   }
   __syncthreads();
-  constexpr int CPR = D / 8;
-  const int n_items = n_tok * r * CPR;
-  for (int c = threadIdx.x; c < n_items; c += kThreads) {
-    const int tt = c / (r * CPR);
-    const int rem = c - tt * r * CPR;
-    const int e = rem / CPR;
-    const int ch = rem - e * CPR;
-    if ((kept[tt] >> e) & 1ull) continue;
-    const size_t off = b * a.o_b + (gam * r + e) * a.o_h + (t_lo + tt) * a.o_t + ch * 8;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    if (a.out_bf16) {
-      __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + off));
-    } else {
-      u32x4* p = reinterpret_cast<u32x4*>(static_cast<float*>(a.out) + off);
-      __builtin_nontemporal_store(z, p);
-      __builtin_nontemporal_store(z, p + 1);
+  // Each wave stores the zero rows of its tokens wave, wave + W, ...: their
+  // masks are read together (one per lane) and handed out with readlane, and
+  // one store instruction covers 64 / CPR rows of a token, 16 bytes per lane.
+  constexpr int CPR = D / 8;             // 16-byte chunks of a bf16 row (8 elements each)
+  constexpr int kHeadsPer = 64 / CPR;    // rows per store instruction
+  static_assert(kRowsPerBlock / W <= 64, "a wave's tokens fit in one mask per lane");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int my_tok = wave + W * lane;
+  const unsigned long long my_mask = my_tok < n_tok ? kept[my_tok] : ~0ull;
+  const unsigned mask_lo = (unsigned)my_mask, mask_hi = (unsigned)(my_mask >> 32);
+  const int e_lane = lane / CPR, ch = lane % CPR;
+  const size_t elt = a.out_bf16 ? 2 : 4;
+  char* const base = static_cast<char*>(a.out) + (b * a.o_b + (size_t)t_lo * a.o_t + (size_t)ch * 8) * elt;
+  const int n_mine = n_tok > wave ? (n_tok - wave + W - 1) / W : 0;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int j = 0; j < n_mine; ++j) {
+    const unsigned long long m = ((unsigned long long)__builtin_amdgcn_readlane(mask_hi, j) << 32) |
+                                 __builtin_amdgcn_readlane(mask_lo, j);
+    char* const tok_base = base + (size_t)(wave + W * j) * a.o_t * elt;
+    for (int e0 = 0; e0 < r; e0 += kHeadsPer) {
+      const int e = e0 + e_lane;
+      if (e < r && !((m >> e) & 1ull)) {
+        u32x4* const p = reinterpret_cast<u32x4*>(tok_base + (size_t)(gam * r + e) * a.o_h * elt);
+        __builtin_nontemporal_store(z, p);
+        if (!a.out_bf16) __builtin_nontemporal_store(z, p + 1);
+      }
     }
   }
 }
