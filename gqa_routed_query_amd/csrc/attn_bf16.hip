@@ -363,13 +363,22 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   // only then let the Q copy start.)
   // The wave's 32 Q rows into QOw by DMA, granule by granule as for K (pad
   // granules receive a copy of granule 0).
+  // The table entries of all the copies are read first, so the copies wait
+  // for one LDS round trip rather than one per batch.
+  int2 qrows[kQDma];
+#pragma unroll
+  for (int j = 0; j < kQDma; ++j) {
+    const int row = min((j * 64 + lane) / L::kGPR, 31);
+    const int4 ri = tab[row];
+    qrows[j] = make_int2(ri.x, ri.y);
+  }
 #pragma unroll
   for (int j = 0; j < kQDma; ++j) {
     const int p = j * 64 + lane;
-    int row = p / L::kGPR, gr = p - row * L::kGPR;
-    if (row > 31) row = 31;
-    if (gr >= L::kCPR) gr = 0;
-    const int4 ri = tab[row];
+    const int row = p / L::kGPR;
+    int gr = p - row * L::kGPR;
+    if (gr >= L::kCPR || row > 31) gr = 0;
+    const int2 ri = qrows[j];
     const uint16_t* src = (shared ? a.q_sh + (size_t)b * a.T * D : a.q + b * a.q_b + (size_t)ri.y * a.q_h) +
                           (size_t)ri.x * D + gr * 8;
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(QOw + j * 512), 16, 0, 0);
