@@ -63,7 +63,12 @@ struct DTile {
   static constexpr int wElems = kElems + vElems;    // one wave's LDS staging area
   static constexpr int kCPR = D / 8;
   static constexpr int kLoads = kSub * kCPR / 64;   // 16-byte loads per lane per sub-block (K or V)
-  static constexpr int kDS = D / 32;                // 32-wide reduction steps for S^T
+  // S^T = K Q^T on 16x16x32 MFMAs: lane group grp (lane / 16) holds d in
+  // [grp * kGS, grp * kGS + 8 * kDS) of its row, in kDS steps of 8. At D = 16
+  // one step covers d < 16 in groups 0 and 1; groups 2 and 3 hold zeros.
+  static constexpr int kDS = D >= 32 ? D / 32 : 1;   // 32-wide reduction steps for S^T
+  static constexpr int kGS = D >= 32 ? D / 4 : 8;    // first d of lane group grp: grp * kGS
+  __device__ static bool group_live(int grp) { return grp * kGS < D; }
 };
 
 struct KArgs {
@@ -176,11 +181,12 @@ __device__ __forceinline__ void load_q(const KArgs& a, const Piece& p, int grp, 
   for (int hb = 0; hb < HB; ++hb) {
     const int e = hb * 16 + i16;
     const int head = head_of<ROUTED>(a, p.b, p.gam, min(e, a.R - 1));
-    const uint16_t* qrow = a.q + ((size_t)p.b * a.h + head) * D + grp * (D / 4);
+    const bool live = DTile<D>::group_live(grp);
+    const uint16_t* qrow = a.q + ((size_t)p.b * a.h + head) * D + (live ? grp * DTile<D>::kGS : 0);
 #pragma unroll
     for (int ds = 0; ds < DTile<D>::kDS; ++ds) {
       bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 8 * ds);
-      if (e >= a.R) x = bf16x8{};
+      if (e >= a.R || !live) x = bf16x8{};
       qf[hb][ds] = x;
     }
   }
@@ -306,7 +312,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int ds = 0; ds < L::kDS; ++ds)
-            kf[kb][ds] = *reinterpret_cast<const bf16x8*>(Kw + (16 * kb + i16) * L::kPitch + grp * (D / 4) + 8 * ds);
+            kf[kb][ds] = L::group_live(grp)
+                             ? *reinterpret_cast<const bf16x8*>(Kw + (16 * kb + i16) * L::kPitch + grp * L::kGS + 8 * ds)
+                             : bf16x8{};
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
@@ -763,15 +771,21 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(KArgs a) {
   }
 }
 
+// 17-32 heads per group run on the 32-column kernel, except at D = 16, whose
+// 16-row O^T fits the 16x16x32 kernel with two head blocks in few registers.
 template <int D>
 const void* kernel_for_hb(int hb) {
   if (hb == 1) return reinterpret_cast<const void*>(&decode_kernel<D, 1, false>);
-  if (hb == 2) return reinterpret_cast<const void*>(&decode32_kernel<D, false>);
+  if (hb == 2) {
+    if constexpr (D == 16) return reinterpret_cast<const void*>(&decode_kernel<D, 2, false>);
+    else return reinterpret_cast<const void*>(&decode32_kernel<D, false>);
+  }
   if (hb <= 4) return reinterpret_cast<const void*>(&decode_kernel<D, 4, false>);
   return nullptr;
 }
 
 const void* decode_kernel_for(int d, int hb) {
+  if (d == 16) return kernel_for_hb<16>(hb);
   if (d == 32) return kernel_for_hb<32>(hb);
   if (d == 64) return kernel_for_hb<64>(hb);
   if (d == 128) return kernel_for_hb<128>(hb);
@@ -782,11 +796,14 @@ template <int D, bool ROUTED>
 hipError_t launch_dr(const KArgs& a, const dim3 grid, hipStream_t stream) {
   const dim3 block(kThreads);
   const int hb = div_up(a.R, 16);
-  if (hb == 1)
+  if (hb == 1) {
     hipLaunchKernelGGL((decode_kernel<D, 1, ROUTED>), grid, block, 0, stream, a);
-  else if (hb == 2)
-    hipLaunchKernelGGL((decode32_kernel<D, ROUTED>), grid, block, 0, stream, a);
-  else if (hb <= 4)
+  } else if (hb == 2) {
+    if constexpr (D == 16)
+      hipLaunchKernelGGL((decode_kernel<D, 2, ROUTED>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode32_kernel<D, ROUTED>), grid, block, 0, stream, a);
+  } else if (hb <= 4)
     hipLaunchKernelGGL((decode_kernel<D, 4, ROUTED>), grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
@@ -824,7 +841,7 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
 
 }  // namespace
 
-bool decode_supports(int d) { return d == 32 || d == 64 || d == 128; }
+bool decode_supports(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 int decode_units(int h, int g, int d) {
   if (const char* env = std::getenv("GQA_DECODE_UNITS")) {
@@ -882,6 +899,7 @@ hipError_t decode_scratch(void** ptr) {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   switch (p.d) {
+    case 16: return launch_d<16>(p, stream);
     case 32: return launch_d<32>(p, stream);
     case 64: return launch_d<64>(p, stream);
     case 128: return launch_d<128>(p, stream);

@@ -91,7 +91,7 @@ def _decode(**kw):
     (dict(h=8, g=3), INVALID),
     (dict(lens=None), INVALID),
     (dict(i=F32), UNSUPPORTED),
-    (dict(d=16), UNSUPPORTED),             # decode takes d in {32, 64, 128}
+    (dict(d=8), UNSUPPORTED),              # decode takes d in {16, 32, 64, 128}
     (dict(d=48), UNSUPPORTED),
     (dict(h=128, g=1), UNSUPPORTED),       # 128 heads per group
     (dict(wsb=0, T=1 << 16), WORKSPACE),

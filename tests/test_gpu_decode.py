@@ -33,6 +33,9 @@ def _run(q, kc, vc, lens, out_dtype=torch.float32):
     (4, 16, 4, 600, 32, torch.float32),      # d = 32, 4 heads per group
     (3, 32, 1, 500, 32, torch.bfloat16),     # d = 32, 32 heads per group (the 32-column kernel)
     (2, 48, 1, 300, 32, torch.float32),      # d = 32, 48 heads per group
+    (4, 16, 4, 600, 16, torch.float32),      # d = 16: half the score MFMA's reduction zeroed
+    (3, 32, 1, 500, 16, torch.bfloat16),     # d = 16, 32 heads per group: two 16-head blocks
+    (2, 48, 1, 300, 16, torch.float32),      # d = 16, 48 heads per group
 ])
 def test_decode_shapes_poisoned_padding(B, h, g, T_max, d, out_dt):
     say(f"decode B={B} h={h} g={g} T_max={T_max} d={d} out={out_dt}")

@@ -43,6 +43,8 @@ def _check(out, idx, gate, q, kc, vc, lens, lg, top_k):
     (2, 32, 1, 300, 128, 20, True, torch.float32),    # 20 of 32 kept: the 32-column kernel
     (3, 16, 4, 500, 32, 2, False, torch.float32),     # d = 32
     (2, 32, 1, 400, 32, 9, True, torch.bfloat16),     # d = 32, 9 of 32 kept
+    (3, 16, 4, 500, 16, 2, False, torch.float32),     # d = 16
+    (2, 32, 1, 300, 16, 5, True, torch.bfloat16),     # d = 16, 5 of 32 kept
 ])
 def test_gqe_decode_shapes_poisoned_padding(B, h, g, T_max, d, top_k, ties, out_dt):
     say(f"gqe decode B={B} h={h} g={g} T_max={T_max} d={d} k={top_k} ties={ties} out={out_dt}")
