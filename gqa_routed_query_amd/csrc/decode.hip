@@ -68,7 +68,7 @@ struct DTile {
   // one step covers d < 16 in groups 0 and 1; groups 2 and 3 hold zeros.
   static constexpr int kDS = D >= 32 ? D / 32 : 1;   // 32-wide reduction steps for S^T
   static constexpr int kGS = D >= 32 ? D / 4 : 8;    // first d of lane group grp: grp * kGS
-  __device__ static bool group_live(int grp) { return grp * kGS < D; }
+  __device__ static bool group_live(int grp) { return D >= 32 || grp * kGS < D; }
 };
 
 struct KArgs {
