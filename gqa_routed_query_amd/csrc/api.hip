@@ -114,7 +114,6 @@ gqa_status prepare_decode(const void* q, const void* k_cache, const void* v_cach
   if (T_max > 0 && (!k_cache || !v_cache)) return fail(GQA_ERR_INVALID_ARG, "null cache pointer");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(GQA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
-  if (in_dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "decode supports bf16 caches only");
   if (!gqa::decode_supports(d)) return fail(GQA_ERR_UNSUPPORTED, "decode supports d in {16, 32, 64, 128}, got %d", d);
   if (h / g > 64) return fail(GQA_ERR_UNSUPPORTED, "decode supports h/g <= 64, got %d", h / g);
   const DecodeLayout L = decode_layout(h, g, d);
@@ -135,6 +134,7 @@ gqa_status prepare_decode(const void* q, const void* k_cache, const void* v_cach
   p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.acc_bytes);
   p.scale = scale;
   p.out_bf16 = out_dtype == GQA_BF16;
+  p.in_f32 = in_dtype == GQA_F32;
   return GQA_OK;
 }
 

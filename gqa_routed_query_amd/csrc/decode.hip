@@ -1,5 +1,6 @@
 // Grouped-query attention decode over a KV cache: one new query token per
-// sequence, bf16 cache, fp32 accumulation, split-K with a log-sum-exp merge.
+// sequence, bf16 cache (fp32 caches: decode_f32_kernel below), fp32
+// accumulation, split-K with a log-sum-exp merge.
 //
 // What is computed (aiunderstanding.org "Attention aux requetes groupees",
 // section "Plongee profonde"; ml-canon "56 GQA / MQA", section on where the
@@ -212,14 +213,15 @@ __device__ __forceinline__ void load_sub(const KArgs& a, const Piece& p, int sb0
 }
 
 // The sub-block of this wave that follows (p, sb) in the block's piece
-// sequence: the next one of the piece, else the wave's first one in a later
-// piece (pieces shorter than 32 * wave keys have none for this wave). pos is
-// the global position of p.k0 and moves along with p. False when the share
-// has no further sub-block for this wave.
+// sequence, for sub-blocks of SUB keys: the next one of the piece, else the
+// wave's first one in a later piece (pieces shorter than SUB * wave keys have
+// none for this wave). pos is the global position of p.k0 and moves along
+// with p. False when the share has no further sub-block for this wave.
+template <int SUB = kSub>
 __device__ __forceinline__ bool next_sub(const KArgs& a, Piece& p, long long& pos, long long end,
                                          int& sb, int& pi, int wave) {
-  if (sb + kWaves * kSub < p.k1) {
-    sb += kWaves * kSub;
+  if (sb + kWaves * SUB < p.k1) {
+    sb += kWaves * SUB;
     return true;
   }
   while (true) {
@@ -227,9 +229,55 @@ __device__ __forceinline__ bool next_sub(const KArgs& a, Piece& p, long long& po
     if (!next_piece(a, p, pos, end, n)) return false;
     p = n;
     ++pi;
-    if (wave * kSub < p.k1) {
-      sb = wave * kSub;
+    if (wave * SUB < p.k1) {
+      sb = wave * SUB;
       return true;
+    }
+  }
+}
+
+// The end of a piece, after each wave has put its (max, sum, accumulator) of
+// heads e0 .. e0+15 in LDS (row wave * 16 + head - e0, pitch D + 4: D values,
+// max, sum): the waves' results merge by log-sum-exp, and the rows go out as
+// output when the piece is the whole stream (whole), else as the partial of
+// slot `slot` of this unit. Rows e >= R are skipped.
+template <int D, bool ROUTED>
+__device__ __forceinline__ void combine_rows(const KArgs& a, const float* comb, const Piece& cur, int e0,
+                                             int unit, int slot, bool whole, int tid) {
+  constexpr int kCP = D + 4;
+  for (int x = tid; x < 16 * D; x += kThreads) {
+    const int hh = x / D;
+    const int d = x - hh * D;
+    const int e = e0 + hh;
+    if (e >= a.R) break;  // x only grows
+    float M = -INFINITY;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, comb[(wv * 16 + hh) * kCP + D]);
+    float acc = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) {
+      const float* src = comb + (wv * 16 + hh) * kCP;
+      const float mw = src[D];
+      const float sc = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
+      acc += sc * src[d];
+      den += sc * src[D + 1];
+    }
+    if (whole) {
+      const int head = head_of<ROUTED>(a, cur.b, cur.gam, e);
+      const size_t off = ((size_t)cur.b * a.h + head) * D + d;
+      float y = acc / den;
+      if (ROUTED) y *= a.gate[((size_t)cur.b * a.g + cur.gam) * a.R + e];
+      if (a.out_bf16)
+        static_cast<uint16_t*>(a.out)[off] = static_cast<uint16_t>(pack_bf16x2(y, 0.0f) & 0xffffu);
+      else
+        static_cast<float*>(a.out)[off] = y;
+    } else {
+      const size_t prow = ((size_t)unit * 2 + slot) * a.R + e;
+      a.part_acc[prow * D + d] = acc;
+      if (d == 0) {
+        a.part_ml[prow * 2 + 0] = M;
+        a.part_ml[prow * 2 + 1] = den;
+      }
     }
   }
 }
@@ -387,46 +435,201 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KArgs a) {
         w[D + 1] = lsum;
       }
       __syncthreads();
-      for (int x = tid; x < 16 * D; x += kThreads) {
-        const int hh = x / D;
-        const int d = x - hh * D;
-        const int e = hb * 16 + hh;
-        if (e >= a.R) break;  // x only grows
-        float M = -INFINITY;
-#pragma unroll
-        for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, comb[(wv * 16 + hh) * kCP + D]);
-        float acc = 0.0f, den = 0.0f;
-#pragma unroll
-        for (int wv = 0; wv < kWaves; ++wv) {
-          const float* src = comb + (wv * 16 + hh) * kCP;
-          const float mw = src[D];
-          const float sc = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
-          acc += sc * src[d];
-          den += sc * src[D + 1];
-        }
-        if (whole) {
-          const int head = head_of<ROUTED>(a, cur.b, cur.gam, e);
-          const size_t off = ((size_t)cur.b * a.h + head) * D + d;
-          float y = acc / den;
-          if (ROUTED) y *= a.gate[((size_t)cur.b * a.g + cur.gam) * a.R + e];
-          if (a.out_bf16)
-            static_cast<uint16_t*>(a.out)[off] = static_cast<uint16_t>(pack_bf16x2(y, 0.0f) & 0xffffu);
-          else
-            static_cast<float*>(a.out)[off] = y;
-        } else {
-          const size_t prow = ((size_t)unit * 2 + slot) * a.R + e;
-          a.part_acc[prow * D + d] = acc;
-          if (d == 0) {
-            a.part_ml[prow * 2 + 0] = M;
-            a.part_ml[prow * 2 + 1] = den;
-          }
-        }
-      }
+      combine_rows<D, ROUTED>(a, comb, cur, hb * 16, unit, slot, whole, tid);
     }
     Piece n;
     if (!next_piece(a, cur, cur_pos, end, n)) break;
     cur = n;
     __syncthreads();  // combine reads done before the staging buffers are rewritten
+  }
+}
+
+// fp32 caches. The shares, pieces and combine of decode_kernel, with the
+// matrix work on v_mfma_f32_16x16x4_f32 (full fp32 operands) and no LDS in the
+// key loop: both operands are loaded from HBM straight into the MFMA lane
+// layout. For lane l = 16 grp + i16 the instruction takes A[i16][grp] and
+// B[grp][i16] and returns rows 4 grp + v (v < 4) of column i16.
+//  * S^T = K Q^T per 16-key sub-block (heads are the 16 columns): MFMA (i, j),
+//    i < D/16, j < 4, reduces over d = 16 i + 4 grp + j, so lane (i16, grp)
+//    reads 4 values at d = 16 i + 4 grp of key row i16 and of its head's
+//    query row; one load instruction covers 64 contiguous bytes of 16 rows.
+//  * O^T += V^T P^T: MFMA (v, db) reduces over keys 4 grp + v -- the keys
+//    whose probabilities lane (i16, grp) holds after the scores -- and its
+//    result row i is d = i * D/16 + db, so lane (i16, grp) reads the D/16
+//    contiguous values at d = i16 * D/16 of V row 4 grp + v.
+// A wave takes 16-key sub-blocks (keys k0 + 16 wave + 64 i of a piece) and
+// loads its next one while the current one is multiplied. One launch covers
+// 16 heads of each group per blockIdx.y (e0 = 16 blockIdx.y), so groups of
+// more than 16 heads read their cache once per 16 heads.
+constexpr int kSubF = 16;
+
+__device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// N contiguous floats at p (16-byte aligned for N >= 4, 8-byte for N == 2),
+// nontemporal: every cached row is read once per call.
+template <int N>
+__device__ __forceinline__ void load_floats_nt(const float* p, float (&x)[N]) {
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[4 * i + j] = t[j];
+    }
+  } else if constexpr (N == 2) {
+    const f32x2 t = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+    x[0] = t[0];
+    x[1] = t[1];
+  } else {
+    x[0] = __builtin_nontemporal_load(p);
+  }
+}
+
+// K and V operands of the 16-key sub-block at sb0 of piece p (rows at or past
+// p.k1 re-read row k1-1 and are masked out of the softmax later).
+template <int D>
+__device__ __forceinline__ void load_sub_f32(const KArgs& a, const Piece& p, int sb0, int grp, int i16,
+                                             float (&kf)[D / 4], float (&vf)[4][D / 16]) {
+  const float* kc = reinterpret_cast<const float*>(a.kc);
+  const float* vc = reinterpret_cast<const float*>(a.vc);
+  const size_t base = ((size_t)p.b * a.g + p.gam) * a.T_max * D;
+  const size_t krow = base + (size_t)min(sb0 + i16, p.k1 - 1) * D;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    float t[4];
+    load_floats_nt<4>(kc + krow + 16 * i + 4 * grp, t);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kf[4 * i + j] = t[j];
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    load_floats_nt<D / 16>(vc + base + (size_t)min(sb0 + 4 * grp + v, p.k1 - 1) * D + i16 * (D / 16), vf[v]);
+}
+
+template <int D, bool ROUTED>
+__global__ __launch_bounds__(kThreads) void decode_f32_kernel(KArgs a) {
+  constexpr int kCP = D + 4;                 // combine row: D values, max, sum, 16-byte pitch
+  __shared__ __attribute__((aligned(16))) float comb[kWaves * 16 * kCP];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int unit = blockIdx.x;
+  const int e0 = 16 * blockIdx.y;  // this block's heads of each group: e0 .. e0+15
+  const long long total = total_keys(a, lane);
+  const long long share = share_of(total, a.n_units);
+  const long long start = (long long)unit * share;
+  if (start >= total) return;  // uniform over the block
+  const long long end = min(start + share, total);
+
+  const int grp = lane >> 4;
+  const int i16 = lane & 15;
+  const float* qs = reinterpret_cast<const float*>(a.q);
+
+  long long cur_pos = start;
+  Piece cur = locate(a, start, end - start, lane);
+  long long ld_pos = cur_pos;
+  Piece ld = cur;
+  int ld_pi = 0, ld_sb = cur.k0 + wave * kSubF;
+  bool ld_ok = ld_sb < cur.k1 || next_sub<kSubF>(a, ld, ld_pos, end, ld_sb, ld_pi, wave);
+  if (ld_sb >= ld.k1) ld_ok = false;
+
+  float kr[D / 4], vr[4][D / 16];
+  if (ld_ok) load_sub_f32<D>(a, ld, ld_sb, grp, i16, kr, vr);
+
+  for (int pi = 0;; ++pi) {
+    // Q^T operand: lane (i16, grp) holds d = 16 i + 4 grp + j of head row e0 + i16.
+    float qf[D / 4];
+    {
+      const int e = e0 + i16;
+      const int head = head_of<ROUTED>(a, cur.b, cur.gam, min(e, a.R - 1));
+      const float* qrow = qs + ((size_t)cur.b * a.h + head) * D;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        float t[4];
+        load_floats_nt<4>(qrow + 16 * i + 4 * grp, t);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qf[4 * i + j] = e < a.R ? t[j] : 0.0f;
+      }
+    }
+    f32x4 o[D / 16];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) o[db] = f32x4{};
+    float m_run = -INFINITY, l_run = 0.0f;
+    const int k1 = cur.k1;
+
+    while (ld_ok && ld_pi == pi) {
+      float kc[D / 4], vc[4][D / 16];
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) kc[i] = kr[i];
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) vc[v][i] = vr[v][i];
+      const int cur_sb = ld_sb;
+      ld_ok = next_sub<kSubF>(a, ld, ld_pos, end, ld_sb, ld_pi, wave);
+      if (ld_ok) load_sub_f32<D>(a, ld, ld_sb, grp, i16, kr, vr);
+
+      // S^T[key][head]: lane holds keys cur_sb + 4 grp + v of head e0 + i16.
+      f32x4 s = f32x4{};
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) s = mfma16x16x4f32(kc[i], qf[i], s);
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (cur_sb + 4 * grp + v >= k1) s[v] = -INFINITY;
+        mloc = fmaxf(mloc, s[v]);
+      }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      const float m_cand = mloc * a.c;
+      // The reference max is raised only when a score exceeds it by more than
+      // 2^kRescale (probabilities stay below 2^kRescale); the final division
+      // by the row sum is exact whatever reference was used.
+      if (__any(m_cand > m_run + kRescale)) {
+        const float m_new = fmaxf(m_run, m_cand);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) o[db] = o[db] * alpha;
+      }
+      float pv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        pv[v] = fast_exp2(fmaf(s[v], a.c, -m_run));
+        l_run += pv[v];
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) o[db] = mfma16x16x4f32(vc[v][db], pv[v], o[db]);
+    }
+
+    // Combine the 4 waves through LDS; rows e0 .. e0+15 go out as output or
+    // as a partial in slot 0 (the share's first piece) or 1 (its last).
+    const bool whole = cur.k0 == 0 && k1 == cur.len;
+    const int slot = pi == 0 ? 0 : 1;
+    float lsum = l_run;
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    __syncthreads();  // the previous piece's combine reads are done
+    float* w = comb + (wave * 16 + i16) * kCP;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) w[(4 * grp + v) * (D / 16) + db] = o[db][v];
+    if (grp == 0) {
+      w[D] = m_run;
+      w[D + 1] = lsum;
+    }
+    __syncthreads();
+    combine_rows<D, ROUTED>(a, comb, cur, e0, unit, slot, whole, tid);
+    Piece n;
+    if (!next_piece(a, cur, cur_pos, end, n)) break;
+    cur = n;
   }
 }
 
@@ -793,20 +996,22 @@ const void* decode_kernel_for(int d, int hb) {
 }
 
 template <int D, bool ROUTED>
-hipError_t launch_dr(const KArgs& a, const dim3 grid, hipStream_t stream) {
+hipError_t launch_dr(const KArgs& a, const dim3 grid, bool in_f32, hipStream_t stream) {
   const dim3 block(kThreads);
   const int hb = div_up(a.R, 16);
-  if (hb == 1) {
+  if (hb > 4) return hipErrorInvalidValue;
+  if (in_f32) {
+    hipLaunchKernelGGL((decode_f32_kernel<D, ROUTED>), dim3(grid.x, hb), block, 0, stream, a);
+  } else if (hb == 1) {
     hipLaunchKernelGGL((decode_kernel<D, 1, ROUTED>), grid, block, 0, stream, a);
   } else if (hb == 2) {
     if constexpr (D == 16)
       hipLaunchKernelGGL((decode_kernel<D, 2, ROUTED>), grid, block, 0, stream, a);
     else
       hipLaunchKernelGGL((decode32_kernel<D, ROUTED>), grid, block, 0, stream, a);
-  } else if (hb <= 4)
+  } else {
     hipLaunchKernelGGL((decode_kernel<D, 4, ROUTED>), grid, block, 0, stream, a);
-  else
-    return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D, ROUTED>), dim3(div_up(a.B * a.h, kWaves)), block, 0,
@@ -836,7 +1041,7 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   a.c = p.scale * kLog2e;
   a.out_bf16 = p.out_bf16;
   const dim3 grid(p.n_units);
-  return p.idx ? launch_dr<D, true>(a, grid, stream) : launch_dr<D, false>(a, grid, stream);
+  return p.idx ? launch_dr<D, true>(a, grid, p.in_f32, stream) : launch_dr<D, false>(a, grid, p.in_f32, stream);
 }
 
 }  // namespace

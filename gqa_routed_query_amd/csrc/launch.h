@@ -72,9 +72,9 @@ struct RouterProjParams {
 };
 
 struct DecodeParams {
-  const void* q;        // [B, h, d] bf16
-  const void* k_cache;  // [B, g, T_max, d] bf16
-  const void* v_cache;  // [B, g, T_max, d] bf16
+  const void* q;        // [B, h, d] bf16, or fp32 with in_f32
+  const void* k_cache;  // [B, g, T_max, d], dtype of q
+  const void* v_cache;  // [B, g, T_max, d], dtype of q
   const int32_t* lens;  // [B] on the device
   void* out;            // [B, h, d]
   float* part_acc;      // [n_units, 2, h/g, d] fp32 workspace
@@ -86,6 +86,7 @@ struct DecodeParams {
   int n_units;          // waves that share the key range
   float scale;
   int out_bf16;
+  int in_f32;           // q and the caches are fp32 (fp32-operand kernel)
 };
 
 hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream);

@@ -124,7 +124,9 @@ size_t gqa_decode_workspace_bytes(int B, int h, int g, int T_max, int d);
  *   workspace: device memory of at least gqa_decode_workspace_bytes(...)
  *           bytes, 16-byte aligned; contents are scratch (no zeroing needed).
  *           Calls that overlap on one workspace race.
- * Supported: in_dtype BF16, d in {16, 32, 64, 128}, h/g <= 64.
+ * Supported: in_dtype BF16 or F32, d in {16, 32, 64, 128}, h/g <= 64. F32
+ * caches run with fp32 operands throughout (fp32 matrix instructions) and
+ * read the cache once per 16 heads of a group.
  * Returns GQA_ERR_WORKSPACE when workspace_bytes is too small.
  */
 gqa_status gqa_decode(const void* q, const void* k_cache, const void* v_cache,

@@ -50,7 +50,8 @@ void check_entry_points() {
   EXPECT(gqa_decode_workspace_bytes(4, 32, 7, 8192, 128) == 0);
   EXPECT(gqa_decode_workspace_bytes(-1, 32, 8, 8192, 128) == 0);
   EXPECT(gqa_decode(P, P, P, PI, P, 4, 32, 8, 8192, 128, GQA_BF16, GQA_BF16, 0.1f, P, ws - 1, nullptr) == GQA_ERR_WORKSPACE);
-  EXPECT(gqa_decode(P, P, P, PI, P, 4, 32, 8, 8192, 128, GQA_F32, GQA_BF16, 0.1f, P, ws, nullptr) == GQA_ERR_UNSUPPORTED);
+  EXPECT(gqa_decode(P, P, P, PI, P, 4, 32, 8, 8192, 128, GQA_F32, GQA_BF16, 0.1f, P, ws, nullptr) == GQA_ERR_NO_DEVICE);
+  EXPECT(gqa_decode(P, P, P, PI, P, 4, 32, 8, 8192, 128, (gqa_dtype)9, GQA_BF16, 0.1f, P, ws, nullptr) == GQA_ERR_INVALID_ARG);
   EXPECT(gqa_decode(P, P, P, PI, P, 4, 32, 8, 8192, 48, GQA_BF16, GQA_BF16, 0.1f, P, ws, nullptr) == GQA_ERR_UNSUPPORTED);
   EXPECT(gqa_decode(P, P, P, nullptr, P, 4, 32, 8, 8192, 128, GQA_BF16, GQA_BF16, 0.1f, P, ws, nullptr) == GQA_ERR_INVALID_ARG);
   EXPECT(gqa_decode(P, P, P, PI, P, 4, 32, 8, -1, 128, GQA_BF16, GQA_BF16, 0.1f, P, ws, nullptr) == GQA_ERR_INVALID_ARG);

@@ -90,7 +90,7 @@ def _decode(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(h=8, g=3), INVALID),
     (dict(lens=None), INVALID),
-    (dict(i=F32), UNSUPPORTED),
+    (dict(i=7), INVALID),                  # not a dtype
     (dict(d=8), UNSUPPORTED),              # decode takes d in {16, 32, 64, 128}
     (dict(d=48), UNSUPPORTED),
     (dict(h=128, g=1), UNSUPPORTED),       # 128 heads per group
@@ -164,7 +164,7 @@ def _gqe_decode(**kw):
     (dict(lg=None), INVALID),
     (dict(gate=None), INVALID),
     (dict(h=8, g=3), INVALID),
-    (dict(i=F32), UNSUPPORTED),
+    (dict(i=7), INVALID),                  # not a dtype
     (dict(wsb=0), WORKSPACE),
 ])
 def test_gqe_decode_rejects(kw, status):
@@ -248,8 +248,10 @@ def test_peak_probes_reject_bad_args():
 def test_valid_calls_report_no_device():
     assert _prefill() == NO_DEVICE
     assert _decode() == NO_DEVICE
+    assert _decode(i=F32, o=F32) == NO_DEVICE      # fp32 caches pass validation
     assert _gqe() == NO_DEVICE
     assert _gqe_decode() == NO_DEVICE
+    assert _gqe_decode(i=F32) == NO_DEVICE
     assert _build() == NO_DEVICE
     assert lib.gqa_peak_hbm_read(P, 16, P, None) == NO_DEVICE
     assert lib.gqa_peak_mfma_bf16(P, 1, P, ctypes.byref(ctypes.c_double(0.0)), None) == NO_DEVICE
@@ -312,7 +314,7 @@ def test_decode_noalloc_checks(monkeypatch):
     rejects, before any HIP call, shapes whose split partials exceed its
     16 MiB static scratch."""
     assert _noalloc(g=7) == INVALID
-    assert _noalloc(i=F32) == UNSUPPORTED
+    assert _noalloc(i=7) == INVALID
     assert _noalloc(d=48) == UNSUPPORTED
     assert _noalloc(B=0) == OK
     monkeypatch.setenv("GQA_DECODE_UNITS", "100000")   # 100000 waves x 2 x 4 heads x 130 floats
@@ -321,3 +323,4 @@ def test_decode_noalloc_checks(monkeypatch):
     if not torch.cuda.is_available():
         monkeypatch.setenv("GQA_DECODE_UNITS", "512")
         assert _noalloc() == NO_DEVICE
+        assert _noalloc(i=F32) == NO_DEVICE

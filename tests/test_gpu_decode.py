@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import TOL_BF16, dev, max_abs, np64, say
+from gpu_util import TOL_BF16, TOL_F32, dev, max_abs, np64, say
 from workloads import WORKLOADS, decode_inputs
 
 pytestmark = pytest.mark.gpu
@@ -49,6 +49,56 @@ def test_decode_shapes_poisoned_padding(B, h, g, T_max, d, out_dt):
     assert torch.isfinite(out).all()
     err = max_abs(out, oracle.gqa_decode_ref(q, kc, vc, lens))
     assert err <= TOL_BF16, err
+
+
+@pytest.mark.parametrize("B,h,g,T_max,d,out_dt", [
+    (5, 8, 2, 1000, 128, torch.float32),     # 4 heads per group
+    (5, 8, 2, 1000, 128, torch.bfloat16),
+    (3, 32, 1, 700, 128, torch.float32),     # MQA: two 16-head blocks of the grid
+    (2, 64, 1, 130, 128, torch.float32),     # 64 heads per group: four blocks
+    (3, 16, 16, 300, 128, torch.float32),    # MHA
+    (4, 16, 2, 400, 64, torch.float32),      # d = 64
+    (3, 24, 1, 500, 32, torch.float32),      # d = 32, 24 heads: the second block half empty
+    (4, 16, 4, 600, 16, torch.float32),      # d = 16
+    (2, 48, 1, 300, 16, torch.bfloat16),     # d = 16, 48 heads per group
+])
+def test_decode_fp32_cache_poisoned_padding(B, h, g, T_max, d, out_dt):
+    """fp32 q and caches: the fp32-operand kernel, at fp32 accuracy."""
+    say(f"decode fp32 cache B={B} h={h} g={g} T_max={T_max} d={d} out={out_dt}")
+    q, kc, vc, lens = decode_inputs(B, h, g, T_max, d, (1, T_max), dtype="f32", seed=310 + h,
+                                    poison_padding=True)
+    lens[0] = T_max
+    lens[-1] = 1
+    kc[0] = kc[0].nan_to_num(0.0)
+    vc[0] = vc[0].nan_to_num(0.0)
+    out = _run(q, kc, vc, lens, out_dt)
+    assert torch.isfinite(out).all()
+    err = max_abs(out, oracle.gqa_decode_ref(q, kc, vc, lens))
+    assert err <= (TOL_F32 if out_dt == torch.float32 else TOL_BF16), err
+
+
+def test_decode_fp32_cache_edge_lengths_and_shares(monkeypatch):
+    """fp32 caches at lengths around the 16-key sub-block and 64-key step
+    boundaries (and an empty sequence), on the default grid and on grids that
+    cut the streams into pieces of different lengths."""
+    lens_list = [0, 1, 15, 16, 17, 63, 64, 65, 255, 256, 511, 512]
+    B = len(lens_list)
+    q, kc, vc, _ = decode_inputs(B, 8, 2, 512, 128, (1, 1), dtype="f32", seed=33)
+    lens = torch.tensor(lens_list, dtype=torch.int32)
+    for b, n in enumerate(lens_list):
+        kc[b, :, n:] = float("nan")
+        vc[b, :, n:] = float("nan")
+    ref = oracle.gqa_decode_ref(q, kc, vc, lens)
+    for units in (None, "1", "7", "300"):
+        say(f"decode fp32 edge lengths, units={units}")
+        if units:
+            monkeypatch.setenv("GQA_DECODE_UNITS", units)
+        else:
+            monkeypatch.delenv("GQA_DECODE_UNITS", raising=False)
+        out = _run(q, kc, vc, lens)
+        assert torch.isfinite(out).all()
+        assert float(out[0].abs().max()) == 0.0
+        assert max_abs(out, ref) <= TOL_F32
 
 
 def test_decode_edge_lengths():

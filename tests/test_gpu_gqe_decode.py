@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import TOL_BF16, TOL_GATE, dev, max_abs, say
+from gpu_util import TOL_BF16, TOL_F32, TOL_GATE, dev, max_abs, say
 from workloads import WORKLOADS, decode_inputs, router_logits
 
 pytestmark = pytest.mark.gpu
@@ -22,12 +22,12 @@ def _run(q, kc, vc, lens, lg, top_k, out_dtype=torch.float32, workspace=None):
     return res
 
 
-def _check(out, idx, gate, q, kc, vc, lens, lg, top_k):
+def _check(out, idx, gate, q, kc, vc, lens, lg, top_k, tol=TOL_BF16):
     ref, ridx, rgate = oracle.gqe_decode_ref(q.cpu(), kc.cpu(), vc.cpu(), lens.cpu(), lg.cpu(), top_k)
     assert np.array_equal(idx.cpu().numpy(), ridx)
     assert max_abs(gate, rgate) <= TOL_GATE
     assert torch.isfinite(out).all()
-    assert max_abs(out, ref) <= TOL_BF16
+    assert max_abs(out, ref) <= tol
     # a row is nonzero iff its head was kept and its sequence has cached keys
     assert torch.equal((out.cpu() != 0).any(-1), torch.from_numpy((ref != 0).any(-1)))
 
@@ -57,6 +57,28 @@ def test_gqe_decode_shapes_poisoned_padding(B, h, g, T_max, d, top_k, ties, out_
     lg = router_logits(B, 1, h, seed=701 + h, ties=ties)[:, 0].contiguous()
     out, idx, gate = _run(q, kc, vc, lens, lg, top_k, out_dt)
     _check(out, idx, gate, q, kc, vc, lens, lg, top_k)
+
+
+@pytest.mark.parametrize("B,h,g,T_max,d,top_k,ties,out_dt", [
+    (5, 8, 2, 1000, 128, 1, False, torch.float32),
+    (5, 8, 2, 1000, 128, 2, True, torch.bfloat16),
+    (2, 64, 1, 130, 128, 40, False, torch.float32),   # 40 of 64 kept: three 16-row blocks
+    (4, 16, 2, 400, 64, 3, True, torch.float32),      # d = 64
+    (3, 16, 4, 500, 16, 2, False, torch.float32),     # d = 16
+])
+def test_gqe_decode_fp32_cache(B, h, g, T_max, d, top_k, ties, out_dt):
+    """fp32 q and caches through the routed decode: fp32 accuracy."""
+    say(f"gqe decode fp32 cache B={B} h={h} g={g} T_max={T_max} d={d} k={top_k} out={out_dt}")
+    q, kc, vc, lens = decode_inputs(B, h, g, T_max, d, (1, T_max), dtype="f32", seed=720 + h + top_k,
+                                    poison_padding=True)
+    lens[0] = T_max
+    lens[-1] = 1
+    kc[0] = kc[0].nan_to_num(0.0)
+    vc[0] = vc[0].nan_to_num(0.0)
+    lg = router_logits(B, 1, h, seed=721 + h, ties=ties)[:, 0].contiguous()
+    out, idx, gate = _run(q, kc, vc, lens, lg, top_k, out_dt)
+    _check(out, idx, gate, q, kc, vc, lens, lg, top_k,
+           tol=TOL_F32 if out_dt == torch.float32 else TOL_BF16)
 
 
 def test_gqe_decode_edge_lengths():
