@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import TOL_BF16, dev, max_abs, say
+from gpu_util import TOL_BF16, TOL_F32, dev, max_abs, say
 from workloads import decode_inputs
 
 pytestmark = pytest.mark.gpu
@@ -50,3 +50,23 @@ def test_noalloc_bf16_out_and_empty_rows():
     assert float(out_na[1].float().abs().max()) == 0.0 and float(out_na[3].float().abs().max()) == 0.0
     ref = oracle.gqa_decode_ref(q.cpu(), kc.cpu(), vc.cpu(), lens.cpu())
     assert max_abs(out_na, ref) <= TOL_BF16
+
+
+def test_noalloc_fp32_cache():
+    """fp32 caches through the static scratch: bit for bit the workspace call,
+    within the fp32 tolerance of the oracle, two calls in a row (the second
+    smaller, 32 heads per group: two 16-head grid rows)."""
+    import gqa_routed_query_amd as gq
+
+    d = dev()
+    for B, h, g, T_max, hd, lr, seed in [(8, 16, 4, 2000, 128, (1, 2000), 904),
+                                         (3, 32, 1, 400, 32, (0, 400), 905)]:
+        say(f"decode noalloc fp32 cache B={B} h={h} g={g} T_max={T_max} d={hd}")
+        q, kc, vc, lens = decode_inputs(B, h, g, T_max, hd, lr, dtype="f32", seed=seed, device=d)
+        out_na = torch.empty(B, h, hd, dtype=torch.float32, device=d)
+        gq.gqa_decode_noalloc(q, kc, vc, lens, out_na)
+        out_ws = gq.gqa_decode(q, kc, vc, lens, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(out_na, out_ws)
+        ref = oracle.gqa_decode_ref(q.cpu(), kc.cpu(), vc.cpu(), lens.cpu())
+        assert max_abs(out_na, ref) <= TOL_F32
