@@ -13,11 +13,14 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(q, k, v, lg, top_k, causal=True, out_dtype=torch.float32, workspace=True):
+    """The routed call into an output filled with NaN beforehand, so every row
+    the launch leaves unwritten (a kept row or a zero row) shows."""
     import gqa_routed_query_amd as gq
 
     d = dev()
+    out = torch.full(q.shape, float("nan"), dtype=out_dtype, device=d)
     res = gq.gqe_routed_prefill(q.to(d), k.to(d), v.to(d), lg.to(d), top_k, causal=causal,
-                                out_dtype=out_dtype, workspace=workspace)
+                                out=out, workspace=workspace)
     torch.cuda.synchronize()
     return res
 
@@ -132,8 +135,12 @@ def test_gqe_key_split_matches_unsplit(B, h, g, T, d, top_k, out_dt):
     say(f"gqe key split B={B} h={h} g={g} T={T} d={d} k={top_k} out={out_dt}")
     assert gq.gqe_workspace_bytes(B, h, g, T, d, top_k) > 0
     q, k, v, lg = gqe_inputs(B, h, g, T, d, "bf16", seed=300 + T, device=dv)
-    a, ia, ga = gq.gqe_routed_prefill(q, k, v, lg, top_k, out_dtype=out_dt, workspace=True)
-    b, ib, gb = gq.gqe_routed_prefill(q, k, v, lg, top_k, out_dtype=out_dt, workspace=None)
+    nan = float("nan")
+    a, ia, ga = gq.gqe_routed_prefill(q, k, v, lg, top_k, out=torch.full(q.shape, nan, dtype=out_dt, device=dv),
+                                      workspace=True)
+    b, ib, gb = gq.gqe_routed_prefill(q, k, v, lg, top_k, out=torch.full(q.shape, nan, dtype=out_dt, device=dv),
+                                      workspace=None)
+    assert not a.isnan().any() and not b.isnan().any()
     torch.cuda.synchronize()
     assert torch.equal(ia, ib) and torch.equal(ga, gb)
     # The same rows are all zero (the heads the router did not keep). Single
