@@ -42,10 +42,12 @@
 //    The row tiles of a causal grid differ in cost (the number of visible key
 //    tiles), and their dispatch order is planned on the host (plan_order).
 #include <algorithm>
+#include <atomic>
 #include <functional>
 #include <map>
 #include <mutex>
 #include <queue>
+#include <random>
 #include <tuple>
 #include <type_traits>
 #include <vector>
@@ -117,12 +119,15 @@ struct KArgs {
   // n_row_tiles-1-i. A slot packs, in one 64-bit word read with one scalar
   // load: its row tile (bits 0-15), key-split point (16-31), part (32-39) and
   // split number sbi (40-47). Part 1 covers key tiles [0, split) of the row
-  // tile, part 2 [split, n_tiles), and each writes its partial result to
-  // workspace slot (sbi * BG + bg) * 2 + part - 1; part 0 covers them all.
+  // tile, part 2 [split, n_tiles); part 0 covers them all. Part 1 writes its
+  // partial result to workspace slot sbi * BG + bg and then sets
+  // ready[sbi * BG + bg] to epoch; part 2 waits for that, merges the partial
+  // into its own result and writes the rows.
   int n_order;
   uint64_t slot[kMaxOrder];
-  uint32_t split_tile[kMaxOrder];  // row tile of split number i (read by the merge kernel)
   float* ws;
+  unsigned long long* ready;
+  unsigned long long epoch;  // unique per launch (top bit set), so stale flags never match
 };
 
 __host__ __device__ inline int slot_tile(uint64_t s) { return (int)(s & 0xffffu); }
@@ -523,14 +528,62 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
 
   // Output: each pass stages D*2 bytes of each of the wave's 32 rows in QOw
   // (all of a bf16 row, half of an fp32 row), then stores them row by row, 16
-  // bytes per lane. A key-split part stores instead its partial result in its
-  // workspace slot: the unnormalised O rows in fp32, then per row the
-  // reference max m_ref and the sum l (rows past the end included).
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const bool partial = part != 0;
-  float* const pws =
-      partial ? a.ws + ((size_t)(slot_sbi(sl) * a.BG + bg) * 2 + part - 1) * ((size_t)kRowsPerBlock * (D + 2))
-              : nullptr;
+  // bytes per lane (part 1 of a split tile: into its workspace slot).
+  float l_tot = l_run + __shfl_xor(l_run, 32);
+  // Key-split row tiles. Part 1 stores its partial result: the unnormalised O
+  // rows in fp32, then per row the reference max m_ref and the sum l (rows
+  // past the end included), and publishes it. Part 2 waits for it, merges it
+  // into its own rows as the online softmax merges two key ranges,
+  //   m = max(m_1, m_2),  w_p = 2^(m_p - m),  O = w_1 O_1 + w_2 O_2,  l = w_1 l_1 + w_2 l_2,
+  // and then writes the rows like an unsplit tile.
+  const bool partial = part == 1;
+  float* const pws = part ? a.ws + (size_t)(slot_sbi(sl) * a.BG + bg) * ((size_t)kRowsPerBlock * (D + 2)) : nullptr;
+  if (part == 2) {
+    unsigned long long* const flag = a.ready + slot_sbi(sl) * a.BG + bg;
+    // Part 1 waits for nothing: it stores its partial as soon as its own key
+    // tiles are done, at most one job after this block (fewer blocks spin here
+    // than there are CUs, so part 1 always finds one). The wait is bounded all
+    // the same (2^20 polls, well over 100 ms), after which the rows are NaN.
+    __shared__ int ready_ok;
+    if (tid == 0) {
+      int ok = 0;
+      for (int it = 0; it < (1 << 20); ++it) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch) {
+          ok = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      // Consumed: cleared, so that a replay of this very launch (same epoch,
+      // e.g. from a captured graph) waits for its own part 1 again.
+      if (ok) __hip_atomic_store(flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ready_ok = ok;
+    }
+    // The barrier orders every wave's reads below after thread 0's acquire
+    // (one cache invalidation for the block, not one per wave).
+    __syncthreads();
+    const int prow = wave * 32 + l32;
+    const float m1 = pws[kRowsPerBlock * D + prow], l1 = pws[kRowsPerBlock * (D + 1) + prow];
+    float4 x[D / 32][4];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        x[db][i4] = *reinterpret_cast<const float4*>(pws + (size_t)prow * D + 32 * db + 8 * i4 + 4 * hq);
+    const float mm = fmaxf(m_ref, m1);
+    const float w2 = ready_ok ? fast_exp2(m_ref - mm) : NAN, w1 = fast_exp2(m1 - mm);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        o[db][4 * i4] = w2 * o[db][4 * i4] + w1 * x[db][i4].x;
+        o[db][4 * i4 + 1] = w2 * o[db][4 * i4 + 1] + w1 * x[db][i4].y;
+        o[db][4 * i4 + 2] = w2 * o[db][4 * i4 + 2] + w1 * x[db][i4].z;
+        o[db][4 * i4 + 3] = w2 * o[db][4 * i4 + 3] + w1 * x[db][i4].w;
+      }
+    l_tot = w2 * l_tot + w1 * l1;
+  }
   if (partial && hq == 0) {
     pws[kRowsPerBlock * D + wave * 32 + l32] = m_ref;
     pws[kRowsPerBlock * (D + 1) + wave * 32 + l32] = l_tot;
@@ -605,69 +658,20 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
       }
     }
   }
+  if (partial) {
+    // Every wave waits for its own partial stores to complete, the barrier
+    // for all waves, and thread 0's release then makes them visible
+    // device-wide before the flag (one cache write-back for the block, not
+    // one per wave). A workgroup barrier alone does not wait for stores.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(a.ready + slot_sbi(sl) * a.BG + bg, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
   // The K/V buffers are free since the last tile's barrier.
   static_assert(L::kElems * 2 >= kRowsPerBlock * 8, "the kept-head masks must fit in a K buffer");
   if (ROUTED && a.zero_unselected && !shared && part <= 1)
     zero_unselected_rows<D, W>(a, b, gam, row0, n_rows, reinterpret_cast<unsigned long long*>(K0));
-}
-
-// Merges the two parts of every key-split row tile. Per row the partial
-// results (m_p, l_p, O_p) over the two key ranges, each taken against its own
-// reference max, combine as the online softmax does within a part:
-//   m = max(m_1, m_2),  w_p = 2^(m_p - m),
-//   O = (w_1 O_1 + w_2 O_2) / (w_1 l_1 + w_2 l_2),
-// then the row's gate and the attention kernel's output layout.
-template <int D, int W, bool ROUTED>
-__global__ __launch_bounds__(256) void split_merge_kernel(KArgs a) {
-  constexpr int kRowsPerBlock = W * 32, kRowsPerSub = 256 / (D / 8), kSubs = kRowsPerBlock / kRowsPerSub;
-  static_assert(kRowsPerBlock % kRowsPerSub == 0, "merge sub-blocks must tile the row tile");
-  const int sub = blockIdx.x % kSubs, sbg = blockIdx.x / kSubs;
-  const int sb = sbg / a.BG, bg = sbg % a.BG;
-  const int tile = a.split_tile[sb];
-  const int b = bg / a.g, gam = bg - b * a.g;  // split launches carry no shared head
-  const int R = a.R, n_rows = a.T * R, row0 = tile * kRowsPerBlock;
-  const float* const p1 = a.ws + (size_t)(sb * a.BG + bg) * 2 * ((size_t)kRowsPerBlock * (D + 2));
-  const float* const p2 = p1 + (size_t)kRowsPerBlock * (D + 2);
-  {
-    const int row = sub * kRowsPerSub + threadIdx.x / (D / 8), ch = threadIdx.x % (D / 8);
-    const int rho = row0 + row;
-    if (rho >= n_rows) return;
-    const float m1 = p1[kRowsPerBlock * D + row], l1 = p1[kRowsPerBlock * (D + 1) + row];
-    const float m2 = p2[kRowsPerBlock * D + row], l2 = p2[kRowsPerBlock * (D + 1) + row];
-    const float m = fmaxf(m1, m2);
-    const float w1 = fast_exp2(m1 - m), w2 = fast_exp2(m2 - m);
-    const int t = rho / R, slot = rho - t * R;
-    int head;
-    float gate = 1.0f;
-    if (ROUTED) {
-      const size_t o = ((size_t)(b * a.T + t) * a.g + gam) * a.R + slot;
-      head = a.idx[o];
-      gate = a.out_slots ? 1.0f : a.gate[o];
-    } else {
-      head = gam * a.r + slot;
-    }
-    const float sc = gate / (w1 * l1 + w2 * l2);
-    const float4* x1 = reinterpret_cast<const float4*>(p1 + (size_t)row * D + ch * 8);
-    const float4* x2 = reinterpret_cast<const float4*>(p2 + (size_t)row * D + ch * 8);
-    const float4 a0 = x1[0], a1 = x1[1], b0 = x2[0], b1 = x2[1];
-    const float v[8] = {(w1 * a0.x + w2 * b0.x) * sc, (w1 * a0.y + w2 * b0.y) * sc,
-                        (w1 * a0.z + w2 * b0.z) * sc, (w1 * a0.w + w2 * b0.w) * sc,
-                        (w1 * a1.x + w2 * b1.x) * sc, (w1 * a1.y + w2 * b1.y) * sc,
-                        (w1 * a1.z + w2 * b1.z) * sc, (w1 * a1.w + w2 * b1.w) * sc};
-    const int oslot = a.out_slots ? gam * a.R + slot : head;
-    const size_t off = b * a.o_b + oslot * a.o_h + t * a.o_t + ch * 8;
-    if (a.out_bf16) {
-      const u32x4 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                       pack_bf16x2(v[6], v[7])};
-      __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + off));
-    } else {
-      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<float*>(a.out) + off);
-      __builtin_nontemporal_store(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                                        __float_as_uint(v[3])}, dst);
-      __builtin_nontemporal_store(u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
-                                        __float_as_uint(v[7])}, dst + 1);
-    }
-  }
 }
 
 void set_order(KArgs& a, const OrderShape& s) {
@@ -682,9 +686,25 @@ void set_order(KArgs& a, const OrderShape& s) {
   for (size_t i = 0; i < v.size(); ++i) {
     a.slot[i] = (uint64_t)v[i].tile | ((uint64_t)v[i].split << 16) | ((uint64_t)v[i].part << 32) |
                 ((uint64_t)v[i].sbi << 40);
-    if (v[i].part == 1) a.split_tile[v[i].sbi] = v[i].tile;
   }
   a.n_order = (int)v.size();
+}
+
+// Partial slots of the key-split tiles: one per split tile and problem, W*32
+// rows of D fp32 values plus (max, sum) per row.
+size_t split_partial_bytes(int cap, int BG, int rows, int d) {
+  return (size_t)cap * BG * rows * (d + 2) * sizeof(float);
+}
+
+// A value no earlier launch of this process used and that uninitialised
+// workspace is most unlikely to hold: a random start with the top bit set,
+// counting up.
+unsigned long long next_epoch() {
+  static std::atomic<unsigned long long> next{[] {
+    std::random_device rd;
+    return (((unsigned long long)rd() << 32) ^ rd()) | (1ull << 63);
+  }()};
+  return next.fetch_add(1) | (1ull << 63);
 }
 
 template <int D, int W, int BN, int OCC>
@@ -694,23 +714,18 @@ hipError_t launch_dw(KArgs a, const AttnParams& p, hipStream_t stream, int n_cu)
       p.split_ws ? split_cap(a.n_row_tiles, W * 32, p.R, p.T, BN, a.BG_main, n_cu) : 0;
   set_order(a, OrderShape{a.n_row_tiles, W * 32, p.R, p.T, BN, a.BG_main, a.BG - a.BG_main, n_cu,
                           a.BG == a.BG_main ? max_split : 0});
+  // Workspace: the partial slots of up to max_split split tiles per problem,
+  // then their ready flags.
   a.ws = static_cast<float*>(p.split_ws);
-  int n_split = 0;
-  for (int i = 0; i < a.n_order; ++i) n_split += slot_part(a.slot[i]) == 1;
+  a.ready = p.split_ws ? reinterpret_cast<unsigned long long*>(static_cast<char*>(p.split_ws) +
+                                                               split_partial_bytes(max_split, a.BG_main, W * 32, D))
+                       : nullptr;
+  a.epoch = p.split_ws ? next_epoch() : 0;
   const dim3 grid((a.n_order ? a.n_order : a.n_row_tiles) * a.BG), block(W * 64);
   if (p.idx)
     hipLaunchKernelGGL((attn_bf16_kernel<D, W, BN, OCC, true>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<D, W, BN, OCC, false>), grid, block, 0, stream, a);
-  if (n_split == 0) return hipGetLastError();
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // One merge block per 256 (row, 8-column chunk) items of a split tile.
-  const dim3 merge_grid(n_split * a.BG * (W * 32 * (D / 8) / 256));
-  if (p.idx)
-    hipLaunchKernelGGL((split_merge_kernel<D, W, true>), merge_grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((split_merge_kernel<D, W, false>), merge_grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -787,7 +802,8 @@ size_t attn_bf16_split_ws_bytes(int B, int g, int T, int d, int R, int causal) {
   const int W = large ? kWavesLarge : kWavesSmall, kBN = large ? kBNLarge : kBNSmall;
   const int n_bands = div_up(T * R, W * 32);
   const int cap = split_cap(n_bands, W * 32, R, T, kBN, BG, n_cu);
-  return (size_t)cap * BG * 2 * (size_t)(W * 32) * (d + 2) * sizeof(float);
+  if (cap == 0) return 0;
+  return split_partial_bytes(cap, BG, W * 32, d) + (size_t)cap * BG * sizeof(unsigned long long);
 }
 
 hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {

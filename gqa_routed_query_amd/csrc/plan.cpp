@@ -46,7 +46,9 @@ int split_cap(int n_bands, int rows, int R, int T, int kBN, int BG, int n_cu) {
     const BandKeys k = band_keys(i, rows, R, T, kBN);
     if (k.split >= 1 && k.n_tiles - k.split >= 1) ++eligible;
   }
-  return std::min(eligible, kMaxOrder - n_bands);
+  // The second part of a split tile waits for the first: with fewer such
+  // blocks than CUs, some CU always stays free to run the first parts.
+  return std::max(0, std::min({eligible, kMaxOrder - n_bands, (n_cu - 1) / std::max(BG, 1)}));
 }
 
 std::vector<Slot> plan_order(const OrderShape& s) {

@@ -14,8 +14,8 @@
 //
 // Key splitting (routed launches given a workspace): when the grid holds less
 // than two blocks per CU, the heaviest row tiles of the upper half of the
-// sequence are split at a key tile into two parts that run as separate jobs,
-// and a second kernel merges their partial results. The split key tile is
+// sequence are split at a key tile into two parts that run as separate jobs;
+// the second part merges the first part's partial result into its own. The split key tile is
 // never past the tile's first token, so every row sees keys in both parts.
 // A split is kept when it shortens the modelled end.
 #pragma once
@@ -57,7 +57,9 @@ struct BandKeys {
 BandKeys band_keys(int i, int rows, int R, int T, int kBN);
 
 // Row tiles that may be split in one launch (0 when the grid has two or more
-// blocks per CU): those of the upper half with a split point inside.
+// blocks per CU): those of the upper half with a split point inside, and fewer
+// than n_cu / BG, so that the second parts (which wait for the first) never
+// hold every CU.
 int split_cap(int n_bands, int rows, int R, int T, int kBN, int BG, int n_cu);
 
 // The planned dispatch order: one slot per band (a whole row tile, or one part

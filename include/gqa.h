@@ -272,11 +272,12 @@ gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v,
  * Bytes of device workspace gqe_routed_prefill can use at this shape (causal
  * bf16 on the current device; 0 when it would use none). With the workspace,
  * a launch whose grid is less than two blocks per CU may split the key range
- * of its heaviest causal row tiles over two jobs whose partial results (the
- * row max, the row sum and the unnormalised output, fp32) are merged by a
- * second kernel: the same result up to rounding (each part rounds its
- * probabilities to bf16 against its own reference maximum), with the work
- * spread over the chip.
+ * of its heaviest causal row tiles over two jobs: the first stores its
+ * partial result (the row max, the row sum and the unnormalised output, fp32)
+ * with a ready flag, and the second merges it into its own and writes the
+ * rows. The same result up to rounding (each part rounds its probabilities
+ * to bf16 against its own reference maximum), with the work spread over the
+ * chip.
  */
 size_t gqe_workspace_bytes(int B, int h, int g, int T, int d, int top_k);
 

@@ -145,6 +145,7 @@ void check_planner() {
                 if (n_bands < 2 || n_bands > gqa::kMaxOrder) continue;
                 const int cap = B_sh ? 0 : gqa::split_cap(n_bands, rows, R, T, kBN, BG, n_cu);
                 EXPECT(cap >= 0 && cap <= gqa::kMaxOrder - n_bands);
+                EXPECT((long long)cap * BG < n_cu);  // waiting second parts never hold every CU
                 check_plan(gqa::OrderShape{n_bands, rows, R, T, kBN, BG, B_sh, n_cu, cap});
                 ++n;
               }

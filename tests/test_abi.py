@@ -130,19 +130,22 @@ def test_gqe_workspace_bytes():
     Without a GPU the size is computed for 256 CUs (MI355X). At k=1 the split
     launch takes the 12-wave grid (384-row tiles: 11 per problem, at most 5 in
     the upper half with a split point)."""
+    def per_split(BG, rows, d):
+        # one split row tile of every problem: part 1's partial result (rows * (d + 2)
+        # floats: O rows, row max, row sum) and its 8-byte ready flag
+        return BG * (rows * (d + 2) * 4 + 8)
+
     small = gq.gqe_workspace_bytes(2, 32, 8, 4096, 128, 1)
     assert small > 0 and small % 16 == 0
-    # one split row tile holds its two partial results: 2 * rows * (d + 2) floats per problem
-    per_tile = 2 * 2 * 8 * 384 * (128 + 2) * 4
-    assert small % per_tile == 0 and small // per_tile <= 6
+    assert small % per_split(16, 384, 128) == 0 and small // per_split(16, 384, 128) <= 6
     # at k=2 the grid takes two rounds of 12-wave blocks: the 8-wave grid (256-row tiles) is split
     k2 = gq.gqe_workspace_bytes(2, 32, 8, 4096, 128, 2)
-    assert k2 == 0 or k2 % (2 * 2 * 8 * 256 * (128 + 2) * 4) == 0
+    assert k2 == 0 or k2 % per_split(16, 256, 128) == 0
     # small split grids keep 12 waves too: B=2, g=2, T=300, k=2 is 600 rows per problem, two
     # 384-row tiles (one in the upper half); B=1, g=4, T=333, d=64, k=3 is 999 rows, three tiles
-    assert gq.gqe_workspace_bytes(2, 8, 2, 300, 128, 2) == 1 * (2 * 2) * 2 * 384 * (128 + 2) * 4
+    assert gq.gqe_workspace_bytes(2, 8, 2, 300, 128, 2) == 1 * per_split(4, 384, 128)
     w = gq.gqe_workspace_bytes(1, 12, 4, 333, 64, 3)
-    assert w > 0 and w % ((1 * 4) * 2 * 384 * (64 + 2) * 4) == 0
+    assert w > 0 and w % per_split(4, 384, 64) == 0
     assert gq.gqe_workspace_bytes(64, 32, 8, 4096, 128, 1) == 0   # 2048+ blocks: no split
     assert gq.gqe_workspace_bytes(2, 32, 8, 4096, 128, 5) == 0    # top_k > h/g
     assert gq.gqe_workspace_bytes(2, 32, 8, 4096, 96, 1) == 0     # d not run on the bf16 kernel

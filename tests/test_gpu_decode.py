@@ -13,10 +13,13 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(q, kc, vc, lens, out_dtype=torch.float32):
+    """The call into an output filled with NaN beforehand, so any element the
+    launch leaves unwritten fails the comparison."""
     import gqa_routed_query_amd as gq
 
     d = dev()
-    out = gq.gqa_decode(q.to(d), kc.to(d), vc.to(d), lens.to(d), out_dtype=out_dtype)
+    out = torch.full(q.shape, float("nan"), dtype=out_dtype, device=d)
+    out = gq.gqa_decode(q.to(d), kc.to(d), vc.to(d), lens.to(d), out=out)
     torch.cuda.synchronize()
     return out
 

@@ -13,11 +13,14 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(q, kc, vc, lens, lg, top_k, out_dtype=torch.float32, workspace=None):
+    """The call into an output filled with NaN beforehand, so any row the
+    launch leaves unwritten (kept or zero) fails the comparison."""
     import gqa_routed_query_amd as gq
 
     d = dev()
+    out = torch.full(q.shape, float("nan"), dtype=out_dtype, device=d)
     res = gq.gqe_routed_decode(q.to(d), kc.to(d), vc.to(d), lens.to(d), lg.to(d), top_k,
-                               out_dtype=out_dtype, workspace=workspace)
+                               out=out, workspace=workspace)
     torch.cuda.synchronize()
     return res
 

@@ -11,11 +11,13 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(q, k, v, causal=True, out_dtype=None, scale=None):
+    """The call into an output filled with NaN beforehand, so any element the
+    launch leaves unwritten fails the comparison."""
     import gqa_routed_query_amd as gq
 
     d = dev()
-    out = gq.gqa_prefill(q.to(d), k.to(d), v.to(d), causal=causal, out_dtype=out_dtype,
-                         scale=scale)
+    out = torch.full(q.shape, float("nan"), dtype=out_dtype or q.dtype, device=d)
+    out = gq.gqa_prefill(q.to(d), k.to(d), v.to(d), causal=causal, out=out, scale=scale)
     torch.cuda.synchronize()
     return out
 
