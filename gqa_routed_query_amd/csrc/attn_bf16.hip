@@ -43,6 +43,7 @@
 //    tiles), and their dispatch order is planned on the host (plan_order).
 #include <algorithm>
 #include <atomic>
+#include <cstdlib>
 #include <functional>
 #include <map>
 #include <mutex>
@@ -128,6 +129,7 @@ struct KArgs {
   float* ws;
   unsigned long long* ready;
   unsigned long long epoch;  // unique per launch (top bit set), so stale flags never match
+  int wait_polls;            // bound of part 2's wait for the flag
 };
 
 __host__ __device__ inline int slot_tile(uint64_t s) { return (int)(s & 0xffffu); }
@@ -543,11 +545,12 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
     // Part 1 waits for nothing: it stores its partial as soon as its own key
     // tiles are done, at most one job after this block (fewer blocks spin here
     // than there are CUs, so part 1 always finds one). The wait is bounded all
-    // the same (2^20 polls, well over 100 ms), after which the rows are NaN.
+    // the same (wait_polls, by default 2^20 polls: well over 100 ms), after
+    // which the rows are NaN.
     __shared__ int ready_ok;
     if (tid == 0) {
       int ok = 0;
-      for (int it = 0; it < (1 << 20); ++it) {
+      for (int it = 0; it < a.wait_polls; ++it) {
         if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch) {
           ok = 1;
           break;
@@ -696,6 +699,17 @@ size_t split_partial_bytes(int cap, int BG, int rows, int d) {
   return (size_t)cap * BG * rows * (d + 2) * sizeof(float);
 }
 
+// Polls of the ready flag before a second part gives up: 2^20, or the
+// GQA_SPLIT_WAIT_POLLS environment variable (0 .. 2^20), which lets tests take
+// the timeout path (NaN rows) with every kernel still ending normally.
+int split_wait_polls() {
+  constexpr long kMax = 1 << 20;
+  const char* env = std::getenv("GQA_SPLIT_WAIT_POLLS");
+  if (!env || !*env) return (int)kMax;
+  const long v = std::strtol(env, nullptr, 10);
+  return (int)(v < 0 ? 0 : v > kMax ? kMax : v);
+}
+
 // A value no earlier launch of this process used and that uninitialised
 // workspace is most unlikely to hold: a random start with the top bit set,
 // counting up.
@@ -721,6 +735,7 @@ hipError_t launch_dw(KArgs a, const AttnParams& p, hipStream_t stream, int n_cu)
                                                                split_partial_bytes(max_split, a.BG_main, W * 32, D))
                        : nullptr;
   a.epoch = p.split_ws ? next_epoch() : 0;
+  a.wait_polls = split_wait_polls();
   const dim3 grid((a.n_order ? a.n_order : a.n_row_tiles) * a.BG), block(W * 64);
   if (p.idx)
     hipLaunchKernelGGL((attn_bf16_kernel<D, W, BN, OCC, true>), grid, block, 0, stream, a);

@@ -277,7 +277,10 @@ gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v,
  * with a ready flag, and the second merges it into its own and writes the
  * rows. The same result up to rounding (each part rounds its probabilities
  * to bf16 against its own reference maximum), with the work spread over the
- * chip.
+ * chip. The second part's wait is bounded; if it runs out (it should not: the
+ * first part waits for nothing), that tile's rows are written as NaN. The
+ * GQA_SPLIT_WAIT_POLLS environment variable (0 .. 2^20, default 2^20) sets
+ * the bound, for tests of that path.
  */
 size_t gqe_workspace_bytes(int B, int h, int g, int T, int d, int top_k);
 

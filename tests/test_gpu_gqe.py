@@ -205,3 +205,87 @@ def test_gqe_sweep_point(B, h, g, T, d, ks, seed):
     assert worst <= TOL_BF16, worst
     del q, k, v, lg, dense
     torch.cuda.empty_cache()
+
+
+def test_gqe_split_wait_timeout_writes_nan(monkeypatch):
+    """The second part of a key-split row tile waits for the first part's
+    partial result with a bounded wait. With the bound set to zero polls
+    (GQA_SPLIT_WAIT_POLLS=0) it gives up at once: every kernel still ends, the
+    split tile's kept rows come out NaN (a loud failure, not a silent one) and
+    every other row equals the normal launch. B=2, h=8, g=2, T=300, k=2: 600
+    rows per (batch, group), two 384-row tiles, the second one split."""
+    import gqa_routed_query_amd as gq
+
+    B, h, g, T, d, top_k = 2, 8, 2, 300, 128, 2
+    dv = dev()
+    say("gqe split wait: timeout path")
+    assert gq.gqe_workspace_bytes(B, h, g, T, d, top_k) > 0
+    q, k, v, lg = gqe_inputs(B, h, g, T, d, "bf16", seed=901, device=dv)
+
+    def call():
+        out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=dv)
+        res = gq.gqe_routed_prefill(q, k, v, lg, top_k, out=out, workspace=True)
+        torch.cuda.synchronize()
+        return res
+
+    ref, ridx, rgate = call()
+    monkeypatch.setenv("GQA_SPLIT_WAIT_POLLS", "0")
+    bad, bidx, bgate = call()
+    monkeypatch.delenv("GQA_SPLIT_WAIT_POLLS")
+    again, aidx, agate = call()
+    assert torch.equal(ridx, bidx) and torch.equal(rgate, bgate)
+    # the launch after the timed-out one is whole again, bit for bit
+    assert torch.equal(again, ref) and torch.equal(aidx, ridx) and torch.equal(agate, rgate)
+    assert not ref.isnan().any()
+    # kept row rho = t*k + j of (b, group) lies in row tile rho // 384
+    idx_c = ridx.cpu()
+    in_split = torch.zeros(B, h, T, dtype=torch.bool)
+    for b in range(B):
+        for t in range(T):
+            for gam in range(g):
+                for j in range(top_k):
+                    in_split[b, int(idx_c[b, t, gam, j]), t] = (t * top_k + j) // 384 == 1
+    bad_c, ref_c = bad.cpu(), ref.cpu()
+    nan_rows = bad_c.isnan().all(-1)
+    assert torch.equal(nan_rows, in_split), int((nan_rows != in_split).sum())
+    assert in_split.any()
+    keep = ~in_split
+    assert torch.equal(bad_c[keep], ref_c[keep])
+
+
+def test_gqe_split_graph_replays():
+    """The key-split launch captured in a HIP graph and replayed with new inputs
+    each time: a replay reuses the captured launch's flag value, so each second
+    part must wait for its own first part (the flag is cleared after use).
+    Every replay equals an eager call on the same inputs, bit for bit, with
+    eager work and synchronisation between the replays. GQE workload shape
+    (B=2, T=4096, h=32, g=8, d=128), k=1."""
+    import gqa_routed_query_amd as gq
+
+    w = WORKLOADS["gqe"]
+    dv = dev()
+    say("gqe split launch in a graph, replays")
+    assert gq.gqe_workspace_bytes(w.B, w.h, w.g, w.T, w.d, 1) > 0
+    q, k, v, lg = gqe_inputs(w.B, w.h, w.g, w.T, w.d, "bf16", seed=950, device=dv)
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gq.gqe_routed_prefill(q, k, v, lg, 1, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, capture_error_mode="relaxed"):
+        _, gidx, ggate = gq.gqe_routed_prefill(q, k, v, lg, 1, out=out)
+    for rep in range(3):
+        q2, k2, v2, lg2 = gqe_inputs(w.B, w.h, w.g, w.T, w.d, "bf16", seed=960 + rep, device=dv)
+        q.copy_(q2), k.copy_(k2), v.copy_(v2), lg.copy_(lg2)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        e_out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=dv)
+        e_out, e_idx, e_gate = gq.gqe_routed_prefill(q, k, v, lg, 1, out=e_out)
+        torch.cuda.synchronize()
+        say(f"graph replay {rep}")
+        assert torch.equal(gidx, e_idx) and torch.equal(ggate, e_gate)
+        assert torch.equal(out, e_out)
