@@ -63,9 +63,10 @@ def parse():
                     help="skip the peak microbenchmarks (HBM read stream, MFMA-only loop)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the sweeps outside the step (KV-group decode, GQE vs GQA over T)")
-    ap.add_argument("--only", choices=["prefill", "decode", "gqe", "sweep", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "gqe", "sweep", "copy", "peaks"], default=None,
                     help="profile helper: run only one kernel family (sweep = the KV-group decode "
-                         "sweep, two calls per g; copy = calibration copy)")
+                         "sweep, two calls per g; copy = calibration copy; peaks = the peak "
+                         "microbenchmarks)")
     return ap.parse_args()
 
 
@@ -140,6 +141,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("copy calibration: 3 copies of 1 GiB")
+        return
+    if args.only == "peaks":
+        # the peak microbenchmarks alone, e.g. for counters on the attention tile loop
+        # (no rocm-smi query: under a profiler, child processes cannot start)
+        measured_peaks(torch, gq, dev, smi=False)
         return
 
     run_prefill = args.only in (None, "prefill")
@@ -482,7 +488,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def measured_peaks(torch, gq, dev):
+def measured_peaks(torch, gq, dev, smi=True):
     """The library's peak microbenchmarks, each timed as the median of 10
     launches with HIP events: an HBM read of a 4 GiB buffer (16 times the
     Infinity Cache), and the MFMA-only loop and the prefill's attention tile
@@ -543,7 +549,7 @@ def measured_peaks(torch, gq, dev):
         f"bf16 MFMA {out['mfma_bf16']['TFLOPs']:.0f} TFLOP/s "
         f"({out['mfma_bf16_sustained']['TFLOPs']:.0f} sustained), attention tile loop "
         f"{out['attn_tile']['TFLOPs']:.0f} TFLOP/s ({out['attn_tile_sustained']['TFLOPs']:.0f} sustained)")
-    out["rocm_smi"] = rocm_smi_clocks()
+    out["rocm_smi"] = rocm_smi_clocks() if smi else None
     return out
 
 
