@@ -337,8 +337,14 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
       if (j >= L::kDma) break;
       const bool isk = j < L::kDmaK;
       const uint32_t off = full ? dma_off[i] : dma_off_last[i];
-      const char* base = reinterpret_cast<const char*>((isk ? kbase : vbase) + (size_t)key0 * D);
-      const uint16_t* src = reinterpret_cast<const uint16_t*>(base + off);
+      // The tile's base address is uniform: kept whole in SGPRs (readfirstlane
+      // hides its parts from reassociation), so the copy takes the scalar-base
+      // form (64-bit base in SGPRs + this lane's 32-bit offset) with no 64-bit
+      // vector address arithmetic per tile.
+      const uint64_t bu = reinterpret_cast<uint64_t>((isk ? kbase : vbase) + (size_t)key0 * D);
+      const uint64_t bs = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32)) << 32) |
+                          (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bu);
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(bs) + off);
       uint16_t* dst = isk ? Kb + j * 512 : Vb + (j - L::kDmaK) * 512;
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
