@@ -200,19 +200,24 @@ __device__ void zero_unselected_rows(const KArgs& a, int b, int gam, int row0, i
   const unsigned mask_lo = (unsigned)my_mask, mask_hi = (unsigned)(my_mask >> 32);
   const int e_lane = lane / CPR, ch = lane % CPR;
   const size_t elt = a.out_bf16 ? 2 : 4;
-  char* const base = static_cast<char*>(a.out) + (b * a.o_b + (size_t)t_lo * a.o_t + (size_t)ch * 8) * elt;
+  // Addresses: each lane's head offset is formed once per group of heads, and
+  // the pointer then steps by a uniform stride from one of the wave's tokens to
+  // the next (no 64-bit multiplies per store).
+  const size_t tok_step = (size_t)W * a.o_t * elt;
+  char* const base =
+      static_cast<char*>(a.out) + (b * a.o_b + (size_t)(t_lo + wave) * a.o_t + (size_t)ch * 8) * elt;
   const int n_mine = n_tok > wave ? (n_tok - wave + W - 1) / W : 0;
   const u32x4 z = {0u, 0u, 0u, 0u};
-  for (int j = 0; j < n_mine; ++j) {
-    const unsigned long long m = ((unsigned long long)__builtin_amdgcn_readlane(mask_hi, j) << 32) |
-                                 __builtin_amdgcn_readlane(mask_lo, j);
-    char* const tok_base = base + (size_t)(wave + W * j) * a.o_t * elt;
-    for (int e0 = 0; e0 < r; e0 += kHeadsPer) {
-      const int e = e0 + e_lane;
-      if (e < r && !((m >> e) & 1ull)) {
-        u32x4* const p = reinterpret_cast<u32x4*>(tok_base + (size_t)(gam * r + e) * a.o_h * elt);
-        __builtin_nontemporal_store(z, p);
-        if (!a.out_bf16) __builtin_nontemporal_store(z, p + 1);
+  for (int e0 = 0; e0 < r; e0 += kHeadsPer) {
+    const int e = e0 + e_lane;
+    const bool mine = e < r;
+    char* p = base + (size_t)(gam * r + (mine ? e : 0)) * a.o_h * elt;
+    for (int j = 0; j < n_mine; ++j, p += tok_step) {
+      const unsigned long long m = ((unsigned long long)__builtin_amdgcn_readlane(mask_hi, j) << 32) |
+                                   __builtin_amdgcn_readlane(mask_lo, j);
+      if (mine && !((m >> e) & 1ull)) {
+        __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(p));
+        if (!a.out_bf16) __builtin_nontemporal_store(z, reinterpret_cast<u32x4*>(p) + 1);
       }
     }
   }
@@ -235,6 +240,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   __shared__ __attribute__((aligned(16))) uint16_t QO[W * kQElems];
   // Per-wave table of the wave's 32 rows: token, head, slot, gate.
   __shared__ int4 rowtab[W * 32];
+  // Per-wave table of the byte offset of each row's output row (from out or
+  // out_sh), formed once with the row.
+  __shared__ long long rowoff_all[W * 32];
 
   const int bid = blockIdx.x;
   const int bg = bid % a.BG;
@@ -303,6 +311,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   uint16_t* const QOw = QO + wave_u * kQElems;
   int4* const tab = rowtab + wave_u * 32;
+  long long* const rowoff = rowoff_all + wave_u * 32;
   const uint16_t* kbase = a.k + b * a.kv_b + gam * a.kv_g;
   const uint16_t* vbase = a.v + b * a.kv_b + gam * a.kv_g;
   // Byte offsets (from the tile's first key row) that this lane loads for the
@@ -361,6 +370,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   if (hq == 0) {
     const RowInfo ri = row_info(min(rho, n_rows - 1));
     tab[l32] = make_int4(ri.t, ri.head, ri.slot, __float_as_int(ri.gate));
+    const int oslot = a.out_slots ? gam * a.R + ri.slot : ri.head;
+    rowoff[l32] = (long long)((shared ? ((size_t)b * a.T + ri.t) * D
+                                      : b * a.o_b + (size_t)oslot * a.o_h + (size_t)ri.t * a.o_t) *
+                              (a.out_bf16 ? 2 : 4));
     // Selecting in the kernel: each (token, slot) entry of idx and gate is
     // written once, by the lane of its row in the block that owns the row's
     // output (the first part of a key-split row tile).
@@ -640,12 +653,12 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
     // the first store, so the reads wait for LDS once rather than per store.
     constexpr int kIt = 32 / kRowsPer;
     u32x4 vs[kIt];
-    int4 rs[kIt];
+    long long rs[kIt];
 #pragma unroll
     for (int i = 0; i < kIt; ++i) {
       const int row = i * kRowsPer + lane / kG;
       vs[i] = *reinterpret_cast<const u32x4_a8*>(stage + row * kRowB + (lane % kG) * 16);
-      rs[i] = tab[row];
+      rs[i] = rowoff[row];
     }
 #pragma unroll
     for (int i = 0; i < kIt; ++i) {
@@ -656,11 +669,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
       if (partial) {
         *reinterpret_cast<u32x4*>(pws + (size_t)(wave * 32 + row) * D + pass * (D / 2) + gran * 4) = v;
       } else if (rr < n_rows) {
-        const int4 ri = rs[i];
-        const int oslot = a.out_slots ? gam * a.R + ri.z : ri.y;
-        const size_t orow = shared ? ((size_t)b * a.T + ri.x) * D : b * a.o_b + oslot * a.o_h + ri.x * a.o_t;
         char* const outp = static_cast<char*>(shared ? a.out_sh : a.out);
-        const size_t ob = orow * (a.out_bf16 ? 2 : 4) + (size_t)pass * D * 2 + gran * 16;
+        const size_t ob = (size_t)rs[i] + (size_t)pass * D * 2 + gran * 16;
         // Nontemporal: the output is not read again here, and streaming it
         // past L2 leaves the K/V tiles that other row tiles reuse in place.
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(outp + ob));
