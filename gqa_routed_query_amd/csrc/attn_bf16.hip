@@ -551,14 +551,20 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
   // (all of a bf16 row, half of an fp32 row), then stores them row by row, 16
   // bytes per lane (part 1 of a split tile: into its workspace slot).
   float l_tot = l_run + __shfl_xor(l_run, 32);
-  // Key-split row tiles. Part 1 stores its partial result: the unnormalised O
-  // rows in fp32, then per row the reference max m_ref and the sum l (rows
-  // past the end included), and publishes it. Part 2 waits for it, merges it
+  // Key-split row tiles. Part 1 stores its partial result: its O rows divided
+  // by their own sum l, rounded to bf16 (half the bytes of fp32 rows, written
+  // and read on the critical path; the rounding is one bf16 step of a convex
+  // combination of values, as for a bf16 output), then per row the reference
+  // max m_ref and the sum l in fp32 (rows past the end included), and
+  // publishes it. Part 2 waits for it, merges it
   // into its own rows as the online softmax merges two key ranges,
-  //   m = max(m_1, m_2),  w_p = 2^(m_p - m),  O = w_1 O_1 + w_2 O_2,  l = w_1 l_1 + w_2 l_2,
+  //   m = max(m_1, m_2),  w_p = 2^(m_p - m),  O = w_1 l_1 (O_1 / l_1) + w_2 O_2,  l = w_1 l_1 + w_2 l_2,
   // and then writes the rows like an unsplit tile.
   const bool partial = part == 1;
-  float* const pws = part ? a.ws + (size_t)(slot_sbi(sl) * a.BG + bg) * ((size_t)kRowsPerBlock * (D + 2)) : nullptr;
+  // Slot layout: kRowsPerBlock bf16 rows of D, then kRowsPerBlock maxima and
+  // kRowsPerBlock sums (fp32): kRowsPerBlock * (D / 2 + 2) floats.
+  constexpr int kMOff = kRowsPerBlock * (D / 2), kLOff = kRowsPerBlock * (D / 2 + 1);
+  float* const pws = part ? a.ws + (size_t)(slot_sbi(sl) * a.BG + bg) * ((size_t)kRowsPerBlock * (D / 2 + 2)) : nullptr;
   if (part == 2) {
     unsigned long long* const flag = a.ready + slot_sbi(sl) * a.BG + bg;
     // Part 1 waits for nothing: it stores its partial as soon as its own key
@@ -586,35 +592,37 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
     // (one cache invalidation for the block, not one per wave).
     __syncthreads();
     const int prow = wave * 32 + l32;
-    const float m1 = pws[kRowsPerBlock * D + prow], l1 = pws[kRowsPerBlock * (D + 1) + prow];
-    float4 x[D / 32][4];
+    const float m1 = pws[kMOff + prow], l1 = pws[kLOff + prow];
+    // Part 1's rows are stored normalised (O_1 / l_1) in bf16.
+    const uint16_t* const p1r = reinterpret_cast<const uint16_t*>(pws) + (size_t)prow * D;
+    uint2 x[D / 32][4];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-        x[db][i4] = *reinterpret_cast<const float4*>(pws + (size_t)prow * D + 32 * db + 8 * i4 + 4 * hq);
+      for (int i4 = 0; i4 < 4; ++i4) x[db][i4] = *reinterpret_cast<const uint2*>(p1r + 32 * db + 8 * i4 + 4 * hq);
     const float mm = fmaxf(m_ref, m1);
     const float w2 = ready_ok ? fast_exp2(m_ref - mm) : NAN, w1 = fast_exp2(m1 - mm);
+    const float w1l = w1 * l1;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        o[db][4 * i4] = w2 * o[db][4 * i4] + w1 * x[db][i4].x;
-        o[db][4 * i4 + 1] = w2 * o[db][4 * i4 + 1] + w1 * x[db][i4].y;
-        o[db][4 * i4 + 2] = w2 * o[db][4 * i4 + 2] + w1 * x[db][i4].z;
-        o[db][4 * i4 + 3] = w2 * o[db][4 * i4 + 3] + w1 * x[db][i4].w;
+        o[db][4 * i4] = w2 * o[db][4 * i4] + w1l * __uint_as_float(x[db][i4].x << 16);
+        o[db][4 * i4 + 1] = w2 * o[db][4 * i4 + 1] + w1l * __uint_as_float(x[db][i4].x & 0xffff0000u);
+        o[db][4 * i4 + 2] = w2 * o[db][4 * i4 + 2] + w1l * __uint_as_float(x[db][i4].y << 16);
+        o[db][4 * i4 + 3] = w2 * o[db][4 * i4 + 3] + w1l * __uint_as_float(x[db][i4].y & 0xffff0000u);
       }
     l_tot = w2 * l_tot + w1 * l1;
   }
   if (partial && hq == 0) {
-    pws[kRowsPerBlock * D + wave * 32 + l32] = m_ref;
-    pws[kRowsPerBlock * (D + 1) + wave * 32 + l32] = l_tot;
+    pws[kMOff + wave * 32 + l32] = m_ref;
+    pws[kLOff + wave * 32 + l32] = l_tot;
   }
-  const float inv = partial ? 1.0f : __int_as_float(tab[l32].w) / l_tot;
+  const float inv = (partial ? 1.0f : __int_as_float(tab[l32].w)) / l_tot;
   constexpr int kG = D * 2 / 16;            // 16-byte granules per staged row
   constexpr int kRowsPer = 64 / kG;         // rows per store instruction
   char* const stage = reinterpret_cast<char*>(QOw);
-  const bool bf16_out = a.out_bf16 && !partial;
+  const bool bf16_out = a.out_bf16 || partial;  // part 1 stores its normalised rows in bf16
   const int n_pass = bf16_out ? 1 : 2;
   // Staged row pitch in bytes. A bf16 row is staged by 8-byte writes, one
   // per lane and row; at an odd multiple of 8 bytes the 32 rows of a write
@@ -667,7 +675,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(OCC))) v
       const u32x4 v = vs[i];
       const int rr = wrow0 + row;
       if (partial) {
-        *reinterpret_cast<u32x4*>(pws + (size_t)(wave * 32 + row) * D + pass * (D / 2) + gran * 4) = v;
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(pws) + (size_t)(wave * 32 + row) * D + gran * 8) = v;
       } else if (rr < n_rows) {
         char* const outp = static_cast<char*>(shared ? a.out_sh : a.out);
         const size_t ob = (size_t)rs[i] + (size_t)pass * D * 2 + gran * 16;
@@ -710,9 +718,9 @@ void set_order(KArgs& a, const OrderShape& s) {
 }
 
 // Partial slots of the key-split tiles: one per split tile and problem, W*32
-// rows of D fp32 values plus (max, sum) per row.
+// rows of D bf16 values plus (max, sum) in fp32 per row.
 size_t split_partial_bytes(int cap, int BG, int rows, int d) {
-  return (size_t)cap * BG * rows * (d + 2) * sizeof(float);
+  return (size_t)cap * BG * rows * (d / 2 + 2) * sizeof(float);
 }
 
 // Polls of the ready flag before a second part gives up: 2^20, or the

@@ -273,10 +273,12 @@ gqa_status gqe_routed_prefill(const void* q, const void* k, const void* v,
  * bf16 on the current device; 0 when it would use none). With the workspace,
  * a launch whose grid is less than two blocks per CU may split the key range
  * of its heaviest causal row tiles over two jobs: the first stores its
- * partial result (the row max, the row sum and the unnormalised output, fp32)
+ * partial result (the row max and row sum in fp32, the output rows divided by
+ * their sum in bf16)
  * with a ready flag, and the second merges it into its own and writes the
  * rows. The same result up to rounding (each part rounds its probabilities
- * to bf16 against its own reference maximum), with the work spread over the
+ * to bf16 against its own reference maximum, and the first part's rows are
+ * rounded to bf16 once), with the work spread over the
  * chip. The second part's wait is bounded; if it runs out (it should not: the
  * first part waits for nothing), that tile's rows are written as NaN. The
  * GQA_SPLIT_WAIT_POLLS environment variable (0 .. 2^20, default 2^20) sets

@@ -131,9 +131,9 @@ def test_gqe_workspace_bytes():
     launch takes the 12-wave grid (384-row tiles: 11 per problem, at most 5 in
     the upper half with a split point)."""
     def per_split(BG, rows, d):
-        # one split row tile of every problem: part 1's partial result (rows * (d + 2)
-        # floats: O rows, row max, row sum) and its 8-byte ready flag
-        return BG * (rows * (d + 2) * 4 + 8)
+        # one split row tile of every problem: part 1's partial result (bf16 rows of d,
+        # fp32 row max and row sum: rows * (d / 2 + 2) floats) and its 8-byte ready flag
+        return BG * (rows * (d // 2 + 2) * 4 + 8)
 
     small = gq.gqe_workspace_bytes(2, 32, 8, 4096, 128, 1)
     assert small > 0 and small % 16 == 0
