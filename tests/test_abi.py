@@ -146,6 +146,9 @@ def test_gqe_workspace_bytes():
     assert gq.gqe_workspace_bytes(2, 8, 2, 300, 128, 2) == 1 * per_split(4, 384, 128)
     w = gq.gqe_workspace_bytes(1, 12, 4, 333, 64, 3)
     assert w > 0 and w % per_split(4, 384, 64) == 0
+    # 170 problems of three 256-row tiles: two tiles have a split point, but the second parts
+    # (which wait for the first) must stay fewer than the 256 CUs, so one split at most
+    assert gq.gqe_workspace_bytes(17, 20, 10, 700, 128, 1) == 1 * per_split(170, 256, 128)
     assert gq.gqe_workspace_bytes(64, 32, 8, 4096, 128, 1) == 0   # 2048+ blocks: no split
     assert gq.gqe_workspace_bytes(2, 32, 8, 4096, 128, 5) == 0    # top_k > h/g
     assert gq.gqe_workspace_bytes(2, 32, 8, 4096, 96, 1) == 0     # d not run on the bf16 kernel

@@ -122,7 +122,9 @@ def test_gqe_large_grid_ragged():
     (2, 32, 8, 4096, 128, 1, torch.bfloat16),   # the GQE workload at k=1: one round of jobs
     (2, 8, 2, 300, 128, 2, torch.float32),
     (1, 12, 4, 333, 64, 3, torch.bfloat16),
-    (1, 12, 4, 333, 64, 3, torch.float32),      # d = 64 with fp32 partials and output
+    (1, 12, 4, 333, 64, 3, torch.float32),      # d = 64 with fp32 output
+    (17, 20, 10, 700, 128, 1, torch.bfloat16),  # 170 problems, 3 row tiles: one split (the cap keeps the
+                                                # 170 waiting second parts below the CU count)
 ])
 def test_gqe_key_split_matches_unsplit(B, h, g, T, d, top_k, out_dt):
     """With a workspace, a causal grid of less than two blocks per CU splits the
